@@ -1,0 +1,170 @@
+"""fp64 CPU oracle for one rank's share of Ulysses sequence parallelism.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg may use it; the product path never imports it. It shares no
+code with the HIP library (it compiles its own C source, ``oracle.c``, with
+gcc + OpenMP into ``liboracle.so`` next to this file).
+
+Functions (each a plain restatement of what the pages describe; the C file
+carries the citations):
+  seq_to_head / head_to_seq   the local pack/unpack around the all-to-all
+  exchange                    the all-to-all itself, as buffer re-indexing
+  attn_fwd                    softmax attention, causal and/or packed docs
+  attn_bwd                    its textbook gradient
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (-O2, OpenMP) into liboracle.so."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        L = ctypes.CDLL(_LIB_PATH)
+        u16p = ctypes.POINTER(ctypes.c_uint16)
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        f64p = ctypes.POINTER(ctypes.c_double)
+        for name in ("orc_seq_to_head", "orc_head_to_seq"):
+            f = getattr(L, name)
+            f.argtypes = [u16p, u16p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, i32p, ctypes.c_int32]
+            f.restype = None
+        L.orc_attn_fwd.argtypes = [f64p, f64p, f64p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_int32, ctypes.c_double, ctypes.c_int32, i32p, ctypes.c_int32,
+                                   i64p, ctypes.c_int64, f64p, f64p]
+        L.orc_attn_fwd.restype = ctypes.c_int
+        L.orc_attn_bwd.argtypes = [f64p, f64p, f64p, f64p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_int32, ctypes.c_double, ctypes.c_int32, i32p, ctypes.c_int32,
+                                   i64p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, f64p, f64p, f64p]
+        L.orc_attn_bwd.restype = ctypes.c_int
+        L.orc_num_threads.argtypes = []
+        L.orc_num_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def num_threads() -> int:
+    return int(lib().orc_num_threads())
+
+
+def _ptr(a: Optional[np.ndarray], ctype):
+    if a is None:
+        return ctypes.POINTER(ctype)()
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact decode of bf16 bit patterns: the 16 bits are the top half of an
+    IEEE binary32 whose low half is zero."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def _as_f64(a: np.ndarray) -> np.ndarray:
+    if a.dtype == np.uint16:
+        return bf16_to_f64(a)
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+# ------------------------------------------------------------------ O1 ----
+
+def seq_to_head(x_seq: np.ndarray, P: int, seg_heads: Sequence[int]) -> np.ndarray:
+    """x_seq [n, H, d] (uint16 bits) -> send [P, n, H/P, d]."""
+    x = np.ascontiguousarray(x_seq, dtype=np.uint16)
+    n, H, d = x.shape
+    assert H == sum(seg_heads) and all(s % P == 0 for s in seg_heads)
+    out = np.empty((P, n, H // P, d), dtype=np.uint16)
+    seg = np.asarray(seg_heads, dtype=np.int32)
+    lib().orc_seq_to_head(_ptr(x, ctypes.c_uint16), _ptr(out, ctypes.c_uint16), n, P, len(seg),
+                          _ptr(seg, ctypes.c_int32), d)
+    return out
+
+
+def head_to_seq(recv: np.ndarray, P: int, seg_heads: Sequence[int]) -> np.ndarray:
+    """recv [P, n, H/P, d] (uint16 bits) -> x_seq [n, H, d]."""
+    x = np.ascontiguousarray(recv, dtype=np.uint16)
+    P_, n, h, d = x.shape
+    assert P_ == P and h * P == sum(seg_heads)
+    out = np.empty((n, h * P, d), dtype=np.uint16)
+    seg = np.asarray(seg_heads, dtype=np.int32)
+    lib().orc_head_to_seq(_ptr(x, ctypes.c_uint16), _ptr(out, ctypes.c_uint16), n, P, len(seg),
+                          _ptr(seg, ctypes.c_int32), d)
+    return out
+
+
+def exchange(sends: Sequence[np.ndarray]) -> list:
+    """The all-to-all as re-indexing: recv_r[s] = send_s[r] for P ranks.
+    sends[s] is rank s's [P, n, h, d] send buffer; returns the P receive
+    buffers, each [P, n, h, d] with source ranks in token order."""
+    P = len(sends)
+    return [np.stack([sends[s][r] for s in range(P)]) for r in range(P)]
+
+
+# ------------------------------------------------------------- O2 / O3 ----
+
+def attn_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: bool = True,
+             cu: Optional[np.ndarray] = None, rows: Optional[np.ndarray] = None
+             ) -> Tuple[np.ndarray, np.ndarray]:
+    """q [N, hq, d], k/v [N, hkv, d] (bf16 bits or floats) -> (o [R, hq, d], lse [hq, R])
+    for the query rows ``rows`` (all N if None), in fp64."""
+    qd, kd, vd = _as_f64(q), _as_f64(k), _as_f64(v)
+    N, hq, d = qd.shape
+    hkv = kd.shape[1]
+    cu_a = None if cu is None else np.ascontiguousarray(cu, dtype=np.int32)
+    rows_a = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    R = N if rows_a is None else len(rows_a)
+    o = np.empty((R, hq, d), dtype=np.float64)
+    lse = np.empty((hq, R), dtype=np.float64)
+    rc = lib().orc_attn_fwd(_ptr(qd, ctypes.c_double), _ptr(kd, ctypes.c_double), _ptr(vd, ctypes.c_double),
+                            N, hq, hkv, d, float(scale), int(bool(causal)), _ptr(cu_a, ctypes.c_int32),
+                            0 if cu_a is None else len(cu_a) - 1, _ptr(rows_a, ctypes.c_int64), R,
+                            _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double))
+    if rc != 0:
+        raise RuntimeError("orc_attn_fwd failed: %d" % rc)
+    return o, lse
+
+
+def attn_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray, scale: float,
+             causal: bool = True, cu: Optional[np.ndarray] = None, rows: Optional[np.ndarray] = None,
+             key_lo: int = 0, key_hi: Optional[int] = None, want_dq: bool = True, want_dkv: bool = True
+             ) -> Tuple[Optional[np.ndarray], Optional[np.ndarray], Optional[np.ndarray]]:
+    """Gradients of L = sum(dout * O): dq [R, hq, d] for ``rows``; dk, dv
+    [key_hi - key_lo, hkv, d] for keys [key_lo, key_hi). fp64."""
+    qd, kd, vd, dod = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
+    N, hq, d = qd.shape
+    hkv = kd.shape[1]
+    key_hi = N if key_hi is None else key_hi
+    cu_a = None if cu is None else np.ascontiguousarray(cu, dtype=np.int32)
+    rows_a = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    R = N if rows_a is None else len(rows_a)
+    dq = np.empty((R, hq, d), dtype=np.float64) if want_dq else None
+    dk = np.empty((key_hi - key_lo, hkv, d), dtype=np.float64) if want_dkv else None
+    dv = np.empty((key_hi - key_lo, hkv, d), dtype=np.float64) if want_dkv else None
+    rc = lib().orc_attn_bwd(_ptr(qd, ctypes.c_double), _ptr(kd, ctypes.c_double), _ptr(vd, ctypes.c_double),
+                            _ptr(dod, ctypes.c_double), N, hq, hkv, d, float(scale), int(bool(causal)),
+                            _ptr(cu_a, ctypes.c_int32), 0 if cu_a is None else len(cu_a) - 1,
+                            _ptr(rows_a, ctypes.c_int64), R, key_lo, key_hi,
+                            _ptr(dq, ctypes.c_double), _ptr(dk, ctypes.c_double), _ptr(dv, ctypes.c_double))
+    if rc != 0:
+        raise RuntimeError("orc_attn_bwd failed: %d" % rc)
+    return dq, dk, dv
