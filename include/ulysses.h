@@ -1,0 +1,189 @@
+/*
+ * libulysses: one GPU's share of Ulysses sequence parallelism on MI355X (gfx950).
+ *
+ * Ulysses splits a sequence of N tokens over P GPUs. Each GPU projects Q, K, V
+ * for its own N/P tokens and all heads; an all-to-all switches the split from
+ * tokens to heads, so each GPU then holds all N tokens of H/P heads and runs
+ * ordinary attention over the full sequence; a second all-to-all switches back
+ * to the token split ("Ulysses sequence parallelism", HF Transformers docs,
+ * intro and its two-GPU diagram; "Ulysses Sequence Parallelism for
+ * Million-Token Context Training", "How Ulysses Sequence Parallelism Works").
+ *
+ * This library provides the per-GPU work around and between the two
+ * exchanges: the local pack/unpack that turns the token-split tensor into the
+ * P per-destination chunks of the all-to-all (and back), and causal
+ * grouped-query attention forward and backward over the full sequence for the
+ * local heads, dense or over packed documents (cu_seqlens).
+ *
+ * Conventions for every call:
+ *  - Tensors are bfloat16 bit patterns (uint16_t), LSE and D are float32.
+ *  - All tensor pointers are device pointers; the caller allocates and owns
+ *    all memory. The library allocates nothing and keeps no mutable global
+ *    state apart from a per-thread error message.
+ *  - Tensor pointers must be 16-byte aligned and token strides must be
+ *    multiples of 8 elements (16 bytes); otherwise ULY_E_ALIGN.
+ *  - Strides are in elements. Within a token row, heads are d elements apart.
+ *  - Calls are asynchronous on `stream` (0 = the null stream). Arguments are
+ *    validated on the host before anything is launched; on any error nothing
+ *    is launched and no output is touched.
+ *  - Return value: ULY_OK (0) or a negative ULY_E_* code.
+ *  - No C++ exception crosses this interface.
+ *  - Batch size is 1; several sequences are expressed as packed documents.
+ */
+#ifndef ULYSSES_H
+#define ULYSSES_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ULY_OK 0
+#define ULY_E_NULL (-1)      /* a required pointer is NULL */
+#define ULY_E_SHAPE (-2)     /* a size is non-positive or too large */
+#define ULY_E_DIV_P (-3)     /* N or a head count is not divisible by P */
+#define ULY_E_GQA (-4)       /* hq is not a multiple of hkv */
+#define ULY_E_HEADDIM (-5)   /* d is not 64 or 128 */
+#define ULY_E_STRIDE (-6)    /* a token stride is smaller than the row it holds */
+#define ULY_E_WORKSPACE (-7) /* workspace missing or too small */
+#define ULY_E_ALIAS (-8)     /* an output overlaps an input where that is not allowed */
+#define ULY_E_HIP (-9)       /* a HIP launch failed; see uly_last_error() */
+#define ULY_E_SEQLENS (-10)  /* cu_seqlens is not 0 = c0 < c1 < ... < c_n = N */
+#define ULY_E_ALIGN (-11)    /* pointer not 16-byte aligned or stride not a multiple of 8 */
+
+/* Text for a status code. Never NULL. */
+const char *uly_status_string(int status);
+
+/* Detail of the last ULY_E_HIP on the calling thread ("" if none). */
+const char *uly_last_error(void);
+
+/*
+ * Tokens per rank for a sequence of N tokens on P ranks: *n_local = N / P.
+ * Sequences must be padded to a multiple of the SP degree ("Ulysses sequence
+ * parallelism", Configure, on sp_size): returns ULY_E_DIV_P when N % P != 0,
+ * ULY_E_SHAPE when N <= 0 or P <= 0, ULY_E_NULL when n_local is NULL.
+ * Host-only.
+ */
+int ulysses_shard_len(int64_t N, int32_t P, int64_t *n_local);
+
+/*
+ * Host-side check of a packed-document offset table (host memory):
+ * cu[0] = 0, strictly increasing, cu[n_seqs] = N. Returns ULY_OK or
+ * ULY_E_SEQLENS (ULY_E_NULL / ULY_E_SHAPE for a NULL table or n_seqs <= 0).
+ * The attention kernels trust their device copy of the table, so callers run
+ * this once when they build it. Packed samples must not attend across their
+ * boundaries ("Ulysses sequence parallelism", Configure, on
+ * sp_attn_implementation).
+ */
+int ulysses_check_cu_seqlens(const int32_t *cu, int32_t n_seqs, int64_t N);
+
+/*
+ * Sequence-to-head pack: the local half of the first all-to-all.
+ *
+ * x_seq  [n_local][H][d]     this rank's tokens with all H = sum(seg_heads)
+ *                            heads, contiguous.
+ * x_send [P][n_local][H/P][d] contiguous; chunk p is what goes to rank p:
+ *                            for every local token, rank p's contiguous block
+ *                            [p*s/P, (p+1)*s/P) of each segment s in order.
+ *                            With seg_heads = {Hq, Hkv, Hkv} (fused q|k|v) a
+ *                            chunk row is [q heads | k heads | v heads] of
+ *                            rank p; with {Hq} it is rank p's query heads.
+ * seg_heads: host array of n_seg (1..8) head counts, each divisible by P
+ *            (the head count must divide by the SP degree: "Ulysses sequence
+ *            parallelism", Configure, the warning on attention heads).
+ * d: head dim, a multiple of 8 (any such value, not only 64/128).
+ * Errors: ULY_E_NULL, ULY_E_SHAPE (n_local, P, d, n_seg out of range),
+ * ULY_E_DIV_P, ULY_E_ALIGN, ULY_E_ALIAS (x_seq and x_send overlap), ULY_E_HIP.
+ * Receiving a chunk from every rank in rank order gives the head shard
+ * [N][H/P][d] with tokens in sequence order (intro diagram: GPU 0 holds the
+ * first tokens).
+ */
+int ulysses_seq_to_head(const uint16_t *x_seq, uint16_t *x_send, int64_t n_local, int32_t P,
+                        int32_t n_seg, const int32_t *seg_heads, int32_t d, hipStream_t stream);
+
+/*
+ * Head-to-sequence unpack: the local half of the second all-to-all, the exact
+ * inverse of ulysses_seq_to_head with the same arguments:
+ * x_recv [P][n_local][H/P][d] (chunk p came from rank p) -> x_seq [n_local][H][d].
+ * In the backward pass the two calls swap roles (the adjoint of a permutation
+ * is its inverse).
+ */
+int ulysses_head_to_seq(const uint16_t *x_recv, uint16_t *x_seq, int64_t n_local, int32_t P,
+                        int32_t n_seg, const int32_t *seg_heads, int32_t d, hipStream_t stream);
+
+/*
+ * Attention forward over the full sequence for the local heads: the local
+ * step between the two exchanges ("How Ulysses Sequence Parallelism Works",
+ * step 4). Exact softmax attention, computed in tiles without an N x N buffer
+ * ("The Challenge of Long Sequence Training": O(n) memory, O(n^2) compute).
+ *
+ * q  [N] rows of hq heads x d, token stride q_stride (elements)
+ * k, v [N] rows of hkv heads x d, token strides k_stride, v_stride
+ *        (q, k, v may be views into one fused [N][hq+2hkv][d] buffer)
+ * o  [N] rows of hq heads x d, token stride o_stride (output, bf16)
+ * lse [hq][N] float32, natural-log log-sum-exp of each row's scaled scores
+ *        (output; kept for the backward pass)
+ * Query head h uses KV head h / (hq / hkv) (contiguous GQA groups).
+ * scale: score multiplier (1/sqrt(d) usually); must be finite and > 0.
+ * causal != 0: key j is visible to query i iff j <= i.
+ * Errors: ULY_E_NULL, ULY_E_SHAPE, ULY_E_GQA, ULY_E_HEADDIM (d not 64/128),
+ * ULY_E_STRIDE (a stride < heads*d), ULY_E_ALIGN, ULY_E_ALIAS (o overlaps q,
+ * k or v), ULY_E_HIP.
+ */
+int attn_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *o, float *lse,
+             int64_t N, int32_t hq, int32_t hkv, int32_t d, int64_t q_stride, int64_t k_stride,
+             int64_t v_stride, int64_t o_stride, float scale, int32_t causal, hipStream_t stream);
+
+/*
+ * attn_fwd over packed documents: key j is visible to query i iff both lie in
+ * the same document [cu[b], cu[b+1]) and (causal == 0 or j <= i).
+ * cu_seqlens: DEVICE int32 [n_seqs + 1], checked by ulysses_check_cu_seqlens
+ * on its host copy (the kernels trust it). max_seqlen: longest document,
+ * used only for validation (must be in [1, N]).
+ */
+int attn_fwd_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *o,
+                    float *lse, int64_t N, int32_t hq, int32_t hkv, int32_t d, int64_t q_stride,
+                    int64_t k_stride, int64_t v_stride, int64_t o_stride, float scale,
+                    int32_t causal, const int32_t *cu_seqlens, int32_t n_seqs,
+                    int32_t max_seqlen, hipStream_t stream);
+
+/* Workspace the backward pass needs (float32 D = rowsum(dO * O), [hq][N]). */
+size_t attn_bwd_workspace_bytes(int64_t N, int32_t hq, int32_t hkv, int32_t d, int32_t n_seqs);
+
+/*
+ * Attention backward: gradients of L = sum(dout * o) for the attn_fwd call
+ * with the same arguments. o and lse are that call's outputs.
+ * dq [N] x hq x d, dk, dv [N] x hkv x d with their own token strides; they
+ * are overwritten (not accumulated). dk and dv sum over the query heads of
+ * each GQA group. dq, dk and dv may be views into one fused
+ * [N][hq+2hkv][d] buffer; none may overlap an input.
+ * ws: device workspace of at least attn_bwd_workspace_bytes(...) bytes,
+ * 256-byte aligned; its contents on entry do not matter.
+ * The result is deterministic (no atomics): the same inputs give the same bits.
+ * Errors: as attn_fwd, plus ULY_E_WORKSPACE.
+ */
+int attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *o,
+             const float *lse, const uint16_t *dout, uint16_t *dq, uint16_t *dk, uint16_t *dv,
+             int64_t N, int32_t hq, int32_t hkv, int32_t d, int64_t q_stride, int64_t k_stride,
+             int64_t v_stride, int64_t o_stride, int64_t do_stride, int64_t dq_stride,
+             int64_t dk_stride, int64_t dv_stride, float scale, int32_t causal, void *ws,
+             size_t ws_bytes, hipStream_t stream);
+
+/* attn_bwd over packed documents (mask as in attn_fwd_varlen). */
+int attn_bwd_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *o,
+                    const float *lse, const uint16_t *dout, uint16_t *dq, uint16_t *dk,
+                    uint16_t *dv, int64_t N, int32_t hq, int32_t hkv, int32_t d,
+                    int64_t q_stride, int64_t k_stride, int64_t v_stride, int64_t o_stride,
+                    int64_t do_stride, int64_t dq_stride, int64_t dk_stride, int64_t dv_stride,
+                    float scale, int32_t causal, const int32_t *cu_seqlens, int32_t n_seqs,
+                    int32_t max_seqlen, void *ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ULYSSES_H */

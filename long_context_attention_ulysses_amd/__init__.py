@@ -1,0 +1,22 @@
+"""One GPU's share of Ulysses sequence parallelism on MI355X (gfx950).
+
+The hot path (layout swaps around the all-to-all, causal GQA attention
+forward and backward, dense or packed documents) runs in libulysses.so,
+hand-written HIP for gfx950; this package is its thin Python binding.
+"""
+from ._lib import (  # noqa: F401
+    EXPORTED,
+    LIB_PATH,
+    STATUS,
+    CODE,
+    UlyssesError,
+    attn_bwd,
+    attn_bwd_workspace_bytes,
+    attn_fwd,
+    raw,
+    status_string,
+    ulysses_check_cu_seqlens,
+    ulysses_head_to_seq,
+    ulysses_seq_to_head,
+    ulysses_shard_len,
+)

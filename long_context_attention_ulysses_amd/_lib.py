@@ -1,0 +1,173 @@
+"""ctypes binding of libulysses.so (C-ABI in include/ulysses.h).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+Tensors are torch device tensors used as plain memory (data_ptr, strides);
+the stream is torch's current HIP stream unless one is given. If the library
+is not built this module raises ImportError: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libulysses.so")
+
+ULY_OK = 0
+STATUS = {
+    -1: "ULY_E_NULL", -2: "ULY_E_SHAPE", -3: "ULY_E_DIV_P", -4: "ULY_E_GQA", -5: "ULY_E_HEADDIM",
+    -6: "ULY_E_STRIDE", -7: "ULY_E_WORKSPACE", -8: "ULY_E_ALIAS", -9: "ULY_E_HIP",
+    -10: "ULY_E_SEQLENS", -11: "ULY_E_ALIGN",
+}
+CODE = {v: k for k, v in STATUS.items()}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libulysses.so is not built (run `python -m long_context_attention_ulysses_amd.build`"
+                      " or __graft_entry__.build())")
+
+# torch ships its own HIP runtime with the same soname as /opt/rocm's. Load it
+# first so libulysses binds to that one runtime: device pointers and streams
+# handed in from torch must belong to the runtime that launches the kernels.
+import torch  # noqa: E402,F401
+
+_L = ctypes.CDLL(LIB_PATH)
+
+_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+_sz = ctypes.c_size_t
+
+_SIGS = {
+    "uly_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "uly_last_error": ([], ctypes.c_char_p),
+    "ulysses_shard_len": ([_i64, _i32, ctypes.POINTER(_i64)], ctypes.c_int),
+    "ulysses_check_cu_seqlens": ([ctypes.POINTER(_i32), _i32, _i64], ctypes.c_int),
+    "ulysses_seq_to_head": ([_p, _p, _i64, _i32, _i32, ctypes.POINTER(_i32), _i32, _p], ctypes.c_int),
+    "ulysses_head_to_seq": ([_p, _p, _i64, _i32, _i32, ctypes.POINTER(_i32), _i32, _p], ctypes.c_int),
+    "attn_fwd": ([_p, _p, _p, _p, _p, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _i64, _f32, _i32, _p],
+                 ctypes.c_int),
+    "attn_fwd_varlen": ([_p, _p, _p, _p, _p, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _i64, _f32, _i32,
+                         _p, _i32, _i32, _p], ctypes.c_int),
+    "attn_bwd_workspace_bytes": ([_i64, _i32, _i32, _i32, _i32], _sz),
+    "attn_bwd": ([_p] * 9 + [_i64, _i32, _i32, _i32] + [_i64] * 8 + [_f32, _i32, _p, _sz, _p], ctypes.c_int),
+    "attn_bwd_varlen": ([_p] * 9 + [_i64, _i32, _i32, _i32] + [_i64] * 8 + [_f32, _i32, _p, _i32, _i32, _p, _sz,
+                                                                          _p], ctypes.c_int),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _f = getattr(_L, _name)
+    _f.argtypes = _args
+    _f.restype = _res
+
+EXPORTED = tuple(_SIGS)
+
+
+class UlyssesError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        detail = _L.uly_status_string(status).decode()
+        if status == CODE["ULY_E_HIP"]:
+            detail += ": " + _L.uly_last_error().decode()
+        super().__init__("%s: %s (%s)" % (where, self.name, detail))
+
+
+def raw():
+    """The ctypes library handle (C names, C argument order)."""
+    return _L
+
+
+def _check(rc: int, where: str):
+    if rc != ULY_OK:
+        raise UlyssesError(rc, where)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return int(stream)
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def status_string(status: int) -> str:
+    return _L.uly_status_string(status).decode()
+
+
+def ulysses_shard_len(N: int, P: int) -> int:
+    out = _i64(0)
+    _check(_L.ulysses_shard_len(N, P, ctypes.byref(out)), "ulysses_shard_len")
+    return out.value
+
+
+def ulysses_check_cu_seqlens(cu: Sequence[int], N: int) -> None:
+    arr = (_i32 * len(cu))(*[int(x) for x in cu])
+    _check(_L.ulysses_check_cu_seqlens(arr, len(cu) - 1, N), "ulysses_check_cu_seqlens")
+
+
+def _seg(seg_heads):
+    return (_i32 * len(seg_heads))(*[int(s) for s in seg_heads])
+
+
+def ulysses_seq_to_head(x_seq, x_send, P: int, seg_heads: Sequence[int], stream=None) -> None:
+    """x_seq [n, H, d] -> x_send [P, n, H/P, d] (contiguous 16-bit tensors)."""
+    n, H, d = x_seq.shape
+    _check(_L.ulysses_seq_to_head(_ptr(x_seq), _ptr(x_send), n, P, len(seg_heads), _seg(seg_heads), d,
+                                  _stream(stream)), "ulysses_seq_to_head")
+
+
+def ulysses_head_to_seq(x_recv, x_seq, P: int, seg_heads: Sequence[int], stream=None) -> None:
+    """x_recv [P, n, H/P, d] -> x_seq [n, H, d] (contiguous 16-bit tensors)."""
+    n, H, d = x_seq.shape
+    _check(_L.ulysses_head_to_seq(_ptr(x_recv), _ptr(x_seq), n, P, len(seg_heads), _seg(seg_heads), d,
+                                  _stream(stream)), "ulysses_head_to_seq")
+
+
+def _tok_stride(t, heads, d):
+    if t.dim() != 3 or t.shape[1] != heads or t.shape[2] != d or t.stride(2) != 1 or t.stride(1) != d:
+        raise ValueError("expected a [N, heads, d] view with unit element stride and head stride d")
+    return t.stride(0)
+
+
+def attn_fwd(q, k, v, o, lse, scale: float, causal: bool = True, cu_seqlens=None,
+             max_seqlen: Optional[int] = None, stream=None) -> None:
+    """q [N, hq, d], k/v [N, hkv, d], o [N, hq, d] (views with any token stride);
+    lse [hq, N] float32. cu_seqlens: int32 device tensor [n_seqs + 1] or None."""
+    N, hq, d = q.shape
+    hkv = k.shape[1]
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), N, hq, hkv, d, _tok_stride(q, hq, d),
+            _tok_stride(k, hkv, d), _tok_stride(v, hkv, d), _tok_stride(o, hq, d), float(scale), int(bool(causal)))
+    if cu_seqlens is None:
+        _check(_L.attn_fwd(*args, _stream(stream)), "attn_fwd")
+    else:
+        n_seqs = cu_seqlens.numel() - 1
+        _check(_L.attn_fwd_varlen(*args, _ptr(cu_seqlens), n_seqs, int(max_seqlen or N), _stream(stream)),
+               "attn_fwd_varlen")
+
+
+def attn_bwd_workspace_bytes(N: int, hq: int, hkv: int, d: int, n_seqs: int = 1) -> int:
+    return int(_L.attn_bwd_workspace_bytes(N, hq, hkv, d, n_seqs))
+
+
+def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, scale: float, causal: bool = True, ws=None,
+             cu_seqlens=None, max_seqlen: Optional[int] = None, stream=None) -> None:
+    """Gradients for attn_fwd with the same q, k, v, scale, mask. ws: device
+    buffer of at least attn_bwd_workspace_bytes(...) bytes, 256-byte aligned."""
+    N, hq, d = q.shape
+    hkv = k.shape[1]
+    n_seqs = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    if ws is None:
+        raise ValueError("attn_bwd needs a workspace tensor")
+    ws_bytes = ws.numel() * ws.element_size()
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+            N, hq, hkv, d, _tok_stride(q, hq, d), _tok_stride(k, hkv, d), _tok_stride(v, hkv, d),
+            _tok_stride(o, hq, d), _tok_stride(dout, hq, d), _tok_stride(dq, hq, d), _tok_stride(dk, hkv, d),
+            _tok_stride(dv, hkv, d), float(scale), int(bool(causal)))
+    if cu_seqlens is None:
+        _check(_L.attn_bwd(*args, _ptr(ws), ws_bytes, _stream(stream)), "attn_bwd")
+    else:
+        _check(_L.attn_bwd_varlen(*args, _ptr(cu_seqlens), n_seqs, int(max_seqlen or N), _ptr(ws), ws_bytes,
+                                  _stream(stream)), "attn_bwd_varlen")

@@ -1,0 +1,290 @@
+// C-ABI of libulysses: argument validation (host only, before any launch),
+// status strings, and dispatch to the kernels. Declarations and the contract
+// of every call are in include/ulysses.h.
+#include <stdio.h>
+#include <string.h>
+
+#include "ulysses.h"
+#include "uly_internal.h"
+
+namespace uly {
+
+static thread_local char g_last_error[256] = "";
+
+int set_hip_error(hipError_t e, const char *where) {
+  snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d)", where, hipGetErrorString(e), (int)e);
+  return ULY_E_HIP;
+}
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [a, a + na) and [b, b + nb) overlap (byte ranges).
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+// Bytes spanned by a strided [rows][width] bf16 view.
+size_t span_bytes(int64_t rows, int64_t stride, int64_t width) {
+  if (rows <= 0) return 0;
+  return (size_t)(((rows - 1) * stride + width) * 2);
+}
+
+int check_swap(const void *src, const void *dst, int64_t n, int32_t P, int32_t nseg,
+               const int32_t *seg, int32_t d) {
+  if (!src || !dst || !seg) return ULY_E_NULL;
+  if (n <= 0 || P <= 0 || nseg <= 0 || nseg > 8 || d <= 0) return ULY_E_SHAPE;
+  if (d % 8 != 0) return ULY_E_ALIGN;
+  int64_t H = 0;
+  for (int s = 0; s < nseg; ++s) {
+    if (seg[s] <= 0) return ULY_E_SHAPE;
+    if (seg[s] % P != 0) return ULY_E_DIV_P;
+    H += seg[s];
+  }
+  // every (token, vector) index of one run must fit the kernel's 32-bit counters
+  if (n * H * d / 8 >= (int64_t)1 << 31) return ULY_E_SHAPE;
+  if (P * nseg > 1 << 16) return ULY_E_SHAPE;
+  if (!aligned16(src) || !aligned16(dst)) return ULY_E_ALIGN;
+  const size_t bytes = (size_t)(n * H * d * 2);
+  if (overlaps(src, bytes, dst, bytes)) return ULY_E_ALIAS;
+  return ULY_OK;
+}
+
+int check_attn_common(const void *q, const void *k, const void *v, int64_t N, int32_t hq,
+                      int32_t hkv, int32_t d, int64_t qs, int64_t ks, int64_t vs, float scale) {
+  if (!q || !k || !v) return ULY_E_NULL;
+  if (N <= 0 || hq <= 0 || hkv <= 0) return ULY_E_SHAPE;
+  if (N >= (int64_t)1 << 31) return ULY_E_SHAPE;  // tile indices are 32-bit
+  if (!(scale > 0.f) || scale > 3.4e38f) return ULY_E_SHAPE;
+  if (hq % hkv != 0) return ULY_E_GQA;
+  if (d != 64 && d != 128) return ULY_E_HEADDIM;
+  if (qs < (int64_t)hq * d || ks < (int64_t)hkv * d || vs < (int64_t)hkv * d) return ULY_E_STRIDE;
+  if (qs % 8 || ks % 8 || vs % 8) return ULY_E_ALIGN;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return ULY_E_ALIGN;
+  return ULY_OK;
+}
+
+int check_out(const void *out, int64_t N, int64_t stride, int64_t width) {
+  if (!out) return ULY_E_NULL;
+  if (stride < width) return ULY_E_STRIDE;
+  if (stride % 8) return ULY_E_ALIGN;
+  if (!aligned16(out)) return ULY_E_ALIGN;
+  (void)N;
+  return ULY_OK;
+}
+
+int check_varlen_args(const int32_t *cu, int32_t n_seqs, int32_t max_seqlen, int64_t N) {
+  if (!cu) return ULY_E_NULL;
+  if (n_seqs <= 0 || n_seqs > N) return ULY_E_SHAPE;
+  if (max_seqlen <= 0 || max_seqlen > N) return ULY_E_SHAPE;
+  return ULY_OK;
+}
+
+int attn_fwd_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *o,
+                  float *lse, int64_t N, int32_t hq, int32_t hkv, int32_t d, int64_t qs,
+                  int64_t ks, int64_t vs, int64_t os, float scale, int32_t causal,
+                  const int32_t *cu, int32_t n_seqs, hipStream_t stream) {
+  int rc = check_attn_common(q, k, v, N, hq, hkv, d, qs, ks, vs, scale);
+  if (rc) return rc;
+  if ((rc = check_out(o, N, os, (int64_t)hq * d))) return rc;
+  if (!lse) return ULY_E_NULL;
+  const size_t ob = span_bytes(N, os, (int64_t)hq * d);
+  if (overlaps(o, ob, q, span_bytes(N, qs, (int64_t)hq * d)) ||
+      overlaps(o, ob, k, span_bytes(N, ks, (int64_t)hkv * d)) ||
+      overlaps(o, ob, v, span_bytes(N, vs, (int64_t)hkv * d)) ||
+      overlaps(lse, (size_t)N * hq * 4, o, ob))
+    return ULY_E_ALIAS;
+  AttnShape s;
+  s.N = N;
+  s.hq = hq;
+  s.hkv = hkv;
+  s.d = d;
+  s.q_stride = qs;
+  s.k_stride = ks;
+  s.v_stride = vs;
+  s.o_stride = os;
+  s.scale = scale;
+  s.causal = causal ? 1 : 0;
+  s.cu = cu;
+  s.n_seqs = n_seqs;
+  return launch_attn_fwd(s, q, k, v, o, lse, stream);
+}
+
+int attn_bwd_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *o,
+                  const float *lse, const uint16_t *dout, uint16_t *dq, uint16_t *dk,
+                  uint16_t *dv, int64_t N, int32_t hq, int32_t hkv, int32_t d, int64_t qs,
+                  int64_t ks, int64_t vs, int64_t os, int64_t dos, int64_t dqs, int64_t dks,
+                  int64_t dvs, float scale, int32_t causal, const int32_t *cu, int32_t n_seqs,
+                  void *ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_attn_common(q, k, v, N, hq, hkv, d, qs, ks, vs, scale);
+  if (rc) return rc;
+  if (!o || !lse || !dout) return ULY_E_NULL;
+  const int64_t wq = (int64_t)hq * d, wk = (int64_t)hkv * d;
+  if (os < wq || dos < wq) return ULY_E_STRIDE;
+  if (os % 8 || dos % 8) return ULY_E_ALIGN;
+  if (!aligned16(o) || !aligned16(dout)) return ULY_E_ALIGN;
+  if ((rc = check_out(dq, N, dqs, wq))) return rc;
+  if ((rc = check_out(dk, N, dks, wk))) return rc;
+  if ((rc = check_out(dv, N, dvs, wk))) return rc;
+  if (!ws) return ULY_E_WORKSPACE;
+  if (ws_bytes < attn_bwd_workspace_bytes(N, hq, hkv, d, n_seqs)) return ULY_E_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return ULY_E_WORKSPACE;
+  // outputs must not overlap any input or the workspace (they may interleave
+  // with each other, as views into one fused buffer)
+  struct R {
+    const void *p;
+    size_t n;
+  };
+  const R ins[] = {{q, span_bytes(N, qs, wq)},     {k, span_bytes(N, ks, wk)},
+                   {v, span_bytes(N, vs, wk)},     {o, span_bytes(N, os, wq)},
+                   {dout, span_bytes(N, dos, wq)}, {lse, (size_t)N * hq * 4},
+                   {ws, (size_t)N * hq * 4}};
+  const R outs[] = {{dq, span_bytes(N, dqs, wq)}, {dk, span_bytes(N, dks, wk)},
+                    {dv, span_bytes(N, dvs, wk)}};
+  for (const R &x : outs)
+    for (const R &y : ins)
+      if (overlaps(x.p, x.n, y.p, y.n)) return ULY_E_ALIAS;
+  AttnShape s;
+  s.N = N;
+  s.hq = hq;
+  s.hkv = hkv;
+  s.d = d;
+  s.q_stride = qs;
+  s.k_stride = ks;
+  s.v_stride = vs;
+  s.o_stride = os;
+  s.scale = scale;
+  s.causal = causal ? 1 : 0;
+  s.cu = cu;
+  s.n_seqs = n_seqs;
+  AttnBwdPtrs p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = dout;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.do_stride = dos;
+  p.dq_stride = dqs;
+  p.dk_stride = dks;
+  p.dv_stride = dvs;
+  p.delta = static_cast<float *>(ws);
+  return launch_attn_bwd(s, p, stream);
+}
+
+}  // namespace
+}  // namespace uly
+
+using namespace uly;
+
+extern "C" {
+
+const char *uly_status_string(int status) {
+  switch (status) {
+    case ULY_OK: return "ok";
+    case ULY_E_NULL: return "null pointer";
+    case ULY_E_SHAPE: return "size out of range";
+    case ULY_E_DIV_P: return "not divisible by the sequence-parallel degree";
+    case ULY_E_GQA: return "query heads not a multiple of KV heads";
+    case ULY_E_HEADDIM: return "unsupported head dim (64 or 128)";
+    case ULY_E_STRIDE: return "token stride smaller than the row";
+    case ULY_E_WORKSPACE: return "workspace missing, misaligned or too small";
+    case ULY_E_ALIAS: return "output overlaps an input";
+    case ULY_E_HIP: return "HIP error";
+    case ULY_E_SEQLENS: return "invalid cu_seqlens";
+    case ULY_E_ALIGN: return "pointer or stride not 16-byte aligned";
+    default: return "unknown status";
+  }
+}
+
+const char *uly_last_error(void) { return g_last_error; }
+
+int ulysses_shard_len(int64_t N, int32_t P, int64_t *n_local) {
+  if (!n_local) return ULY_E_NULL;
+  if (N <= 0 || P <= 0) return ULY_E_SHAPE;
+  if (N % P != 0) return ULY_E_DIV_P;
+  *n_local = N / P;
+  return ULY_OK;
+}
+
+int ulysses_check_cu_seqlens(const int32_t *cu, int32_t n_seqs, int64_t N) {
+  if (!cu) return ULY_E_NULL;
+  if (n_seqs <= 0 || N <= 0) return ULY_E_SHAPE;
+  if (cu[0] != 0 || (int64_t)cu[n_seqs] != N) return ULY_E_SEQLENS;
+  for (int32_t i = 0; i < n_seqs; ++i)
+    if (cu[i + 1] <= cu[i]) return ULY_E_SEQLENS;
+  return ULY_OK;
+}
+
+int ulysses_seq_to_head(const uint16_t *x_seq, uint16_t *x_send, int64_t n_local, int32_t P,
+                        int32_t n_seg, const int32_t *seg_heads, int32_t d, hipStream_t stream) {
+  int rc = check_swap(x_seq, x_send, n_local, P, n_seg, seg_heads, d);
+  if (rc) return rc;
+  return launch_swap(true, x_seq, x_send, n_local, P, n_seg, seg_heads, d, stream);
+}
+
+int ulysses_head_to_seq(const uint16_t *x_recv, uint16_t *x_seq, int64_t n_local, int32_t P,
+                        int32_t n_seg, const int32_t *seg_heads, int32_t d, hipStream_t stream) {
+  int rc = check_swap(x_recv, x_seq, n_local, P, n_seg, seg_heads, d);
+  if (rc) return rc;
+  return launch_swap(false, x_recv, x_seq, n_local, P, n_seg, seg_heads, d, stream);
+}
+
+int attn_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *o, float *lse,
+             int64_t N, int32_t hq, int32_t hkv, int32_t d, int64_t q_stride, int64_t k_stride,
+             int64_t v_stride, int64_t o_stride, float scale, int32_t causal, hipStream_t stream) {
+  return attn_fwd_impl(q, k, v, o, lse, N, hq, hkv, d, q_stride, k_stride, v_stride, o_stride,
+                       scale, causal, nullptr, 0, stream);
+}
+
+int attn_fwd_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *o,
+                    float *lse, int64_t N, int32_t hq, int32_t hkv, int32_t d, int64_t q_stride,
+                    int64_t k_stride, int64_t v_stride, int64_t o_stride, float scale,
+                    int32_t causal, const int32_t *cu_seqlens, int32_t n_seqs,
+                    int32_t max_seqlen, hipStream_t stream) {
+  int rc = check_varlen_args(cu_seqlens, n_seqs, max_seqlen, N);
+  if (rc) return rc;
+  return attn_fwd_impl(q, k, v, o, lse, N, hq, hkv, d, q_stride, k_stride, v_stride, o_stride,
+                       scale, causal, cu_seqlens, n_seqs, stream);
+}
+
+size_t attn_bwd_workspace_bytes(int64_t N, int32_t hq, int32_t hkv, int32_t d, int32_t n_seqs) {
+  (void)hkv;
+  (void)d;
+  (void)n_seqs;
+  if (N <= 0 || hq <= 0) return 0;
+  const size_t bytes = (size_t)N * (size_t)hq * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+int attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *o,
+             const float *lse, const uint16_t *dout, uint16_t *dq, uint16_t *dk, uint16_t *dv,
+             int64_t N, int32_t hq, int32_t hkv, int32_t d, int64_t q_stride, int64_t k_stride,
+             int64_t v_stride, int64_t o_stride, int64_t do_stride, int64_t dq_stride,
+             int64_t dk_stride, int64_t dv_stride, float scale, int32_t causal, void *ws,
+             size_t ws_bytes, hipStream_t stream) {
+  return attn_bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, N, hq, hkv, d, q_stride, k_stride,
+                       v_stride, o_stride, do_stride, dq_stride, dk_stride, dv_stride, scale,
+                       causal, nullptr, 0, ws, ws_bytes, stream);
+}
+
+int attn_bwd_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *o,
+                    const float *lse, const uint16_t *dout, uint16_t *dq, uint16_t *dk,
+                    uint16_t *dv, int64_t N, int32_t hq, int32_t hkv, int32_t d,
+                    int64_t q_stride, int64_t k_stride, int64_t v_stride, int64_t o_stride,
+                    int64_t do_stride, int64_t dq_stride, int64_t dk_stride, int64_t dv_stride,
+                    float scale, int32_t causal, const int32_t *cu_seqlens, int32_t n_seqs,
+                    int32_t max_seqlen, void *ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_varlen_args(cu_seqlens, n_seqs, max_seqlen, N);
+  if (rc) return rc;
+  return attn_bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, N, hq, hkv, d, q_stride, k_stride,
+                       v_stride, o_stride, do_stride, dq_stride, dk_stride, dv_stride, scale,
+                       causal, cu_seqlens, n_seqs, ws, ws_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,120 @@
+"""The C-ABI library loads, exports every symbol include/ulysses.h declares,
+and rejects bad arguments on the host before touching a device (no GPU
+needed: every call here fails validation)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ulysses.h")
+
+uly = pytest.importorskip("long_context_attention_ulysses_amd")
+L = uly.raw()
+
+A = 1 << 20           # a fake, 16-byte aligned "device" address (never dereferenced)
+B = 2 << 20
+C = 3 << 20
+D_ = 4 << 20
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"if", "defined"})
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert set(names) == set(uly.EXPORTED), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for code, name in uly.STATUS.items():
+        assert uly.status_string(code) and uly.status_string(code) != "unknown status", name
+    assert uly.status_string(0) == "ok"
+    assert uly.status_string(-999) == "unknown status"
+
+
+def test_shard_len_and_cu_seqlens():
+    assert uly.ulysses_shard_len(65536, 4) == 16384
+    with pytest.raises(uly.UlyssesError) as e:
+        uly.ulysses_shard_len(65537, 4)
+    assert e.value.name == "ULY_E_DIV_P"
+    with pytest.raises(uly.UlyssesError):
+        uly.ulysses_shard_len(0, 4)
+    uly.ulysses_check_cu_seqlens([0, 5, 6, 10], 10)
+    for bad in ([1, 5, 10], [0, 5, 5, 10], [0, 5, 9], [0, 7, 3, 10]):
+        with pytest.raises(uly.UlyssesError) as e:
+            uly.ulysses_check_cu_seqlens(bad, 10)
+        assert e.value.name == "ULY_E_SEQLENS"
+
+
+def _seg(*s):
+    return (ctypes.c_int32 * len(s))(*s)
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, B, 16, 4, 3, _seg(32, 8, 8), 128), "ULY_E_NULL"),
+    ((A, B, 0, 4, 3, _seg(32, 8, 8), 128), "ULY_E_SHAPE"),
+    ((A, B, 16, 4, 3, _seg(32, 6, 8), 128), "ULY_E_DIV_P"),
+    ((A, B, 16, 4, 3, _seg(32, 8, 8), 100), "ULY_E_ALIGN"),
+    ((A + 2, B, 16, 4, 3, _seg(32, 8, 8), 128), "ULY_E_ALIGN"),
+    ((A, A + 64, 16, 4, 3, _seg(32, 8, 8), 128), "ULY_E_ALIAS"),
+    ((A, B, 16, 4, 9, _seg(*([4] * 9)), 128), "ULY_E_SHAPE"),
+])
+def test_swap_validation(args, code):
+    for fn in (L.ulysses_seq_to_head, L.ulysses_head_to_seq):
+        assert fn(*args, None) == uly.CODE[code]
+
+
+def _fwd(**kw):
+    a = dict(q=A, k=B, v=C, o=D_, lse=5 << 20, N=1024, hq=8, hkv=2, d=128, qs=1536, ks=1536, vs=1536,
+             os=1024, scale=0.088, causal=1)
+    a.update(kw)
+    return L.attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["N"], a["hq"], a["hkv"], a["d"], a["qs"],
+                      a["ks"], a["vs"], a["os"], a["scale"], a["causal"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), "ULY_E_NULL"),
+    (dict(lse=0), "ULY_E_NULL"),
+    (dict(N=0), "ULY_E_SHAPE"),
+    (dict(hkv=3), "ULY_E_GQA"),
+    (dict(d=96, qs=96 * 12, ks=96 * 12, vs=96 * 12, os=96 * 8), "ULY_E_HEADDIM"),
+    (dict(qs=1000), "ULY_E_STRIDE"),
+    (dict(os=1000), "ULY_E_STRIDE"),
+    (dict(qs=1540), "ULY_E_ALIGN"),
+    (dict(k=B + 8), "ULY_E_ALIGN"),
+    (dict(scale=0.0), "ULY_E_SHAPE"),
+    (dict(scale=float("nan")), "ULY_E_SHAPE"),
+    (dict(o=A), "ULY_E_ALIAS"),
+])
+def test_attn_fwd_validation(kw, code):
+    assert _fwd(**kw) == uly.CODE[code]
+
+
+def test_attn_varlen_and_bwd_validation():
+    r = L.attn_fwd_varlen(A, B, C, D_, 5 << 20, 1024, 8, 2, 128, 1536, 1536, 1536, 1024, 0.1, 1, None, 3, 512,
+                          None)
+    assert r == uly.CODE["ULY_E_NULL"]
+    r = L.attn_fwd_varlen(A, B, C, D_, 5 << 20, 1024, 8, 2, 128, 1536, 1536, 1536, 1024, 0.1, 1, 6 << 20, 0, 512,
+                          None)
+    assert r == uly.CODE["ULY_E_SHAPE"]
+    N, hq, hkv, d = 1024, 8, 2, 128
+    need = L.attn_bwd_workspace_bytes(N, hq, hkv, d, 1)
+    assert need >= N * hq * 4 and need % 256 == 0
+
+    def bwd(ws=7 << 20, ws_bytes=need, dq=8 << 20, dk=9 << 20, dv=10 << 20):
+        return L.attn_bwd(A, B, C, D_, 5 << 20, 6 << 20, dq, dk, dv, N, hq, hkv, d, 1536, 1536, 1536, 1024, 1024,
+                          1536, 1536, 1536, 0.1, 1, ws, ws_bytes, None)
+
+    assert bwd(ws=0) == uly.CODE["ULY_E_WORKSPACE"]
+    assert bwd(ws_bytes=need - 1) == uly.CODE["ULY_E_WORKSPACE"]
+    assert bwd(ws=(7 << 20) + 16) == uly.CODE["ULY_E_WORKSPACE"]
+    assert bwd(dq=A) == uly.CODE["ULY_E_ALIAS"]
+    assert bwd(dk=7 << 20) == uly.CODE["ULY_E_ALIAS"]
+    assert bwd(dv=0) == uly.CODE["ULY_E_NULL"]

@@ -1,0 +1,295 @@
+"""GPU parity of attention forward/backward against the fp64 oracle, plus
+invariants checked on the GPU results themselves (determinism, causality,
+head-shard concatenation, single-document varlen == dense)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests._gpu import (FWD_MAX_ABS, FWD_REL, GRAD_MAX_ABS, GRAD_REL, LSE_MAX_ABS, assert_close, dev,
+                        f64, host, sentinel)
+
+pytestmark = pytest.mark.gpu
+
+uly = pytest.importorskip("long_context_attention_ulysses_amd")
+
+
+class Run:
+    """One attention problem on the GPU with q|k|v fused along the head axis
+    ([N, hq + 2 hkv, d], the head shard the all-to-all delivers) and
+    dq|dk|dv written into one fused gradient buffer."""
+
+    def __init__(self, qkv_bits, hq, hkv, scale, causal=True, cu=None):
+        self.N, ht, self.d = qkv_bits.shape
+        assert ht == hq + 2 * hkv
+        self.hq, self.hkv, self.scale, self.causal = hq, hkv, scale, causal
+        self.cu = cu
+        self.qkv = dev(qkv_bits)
+        self.q = self.qkv[:, :hq]
+        self.k = self.qkv[:, hq:hq + hkv]
+        self.v = self.qkv[:, hq + hkv:]
+        self.cu_dev = None if cu is None else torch.tensor(np.asarray(cu, dtype=np.int32), device="cuda")
+        self.max_seqlen = None if cu is None else int(np.max(np.diff(cu)))
+
+    def fwd(self):
+        self.o = sentinel((self.N, self.hq, self.d))
+        self.lse = torch.full((self.hq, self.N), float("nan"), dtype=torch.float32, device="cuda")
+        uly.attn_fwd(self.q, self.k, self.v, self.o, self.lse, self.scale, self.causal, self.cu_dev,
+                     self.max_seqlen)
+        torch.cuda.synchronize()
+        return host(self.o), self.lse.cpu().numpy()
+
+    def bwd(self, dy_bits):
+        self.dy = dev(dy_bits)
+        dqkv = sentinel((self.N, self.hq + 2 * self.hkv, self.d))
+        dq, dk, dv = dqkv[:, :self.hq], dqkv[:, self.hq:self.hq + self.hkv], dqkv[:, self.hq + self.hkv:]
+        nb = uly.attn_bwd_workspace_bytes(self.N, self.hq, self.hkv, self.d)
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        uly.attn_bwd(self.q, self.k, self.v, self.o, self.lse, self.dy, dq, dk, dv, self.scale, self.causal, ws,
+                     self.cu_dev, self.max_seqlen)
+        torch.cuda.synchronize()
+        b = host(dqkv)
+        return b[:, :self.hq], b[:, self.hq:self.hq + self.hkv], b[:, self.hq + self.hkv:]
+
+
+def _split(qkv_bits, hq, hkv):
+    return qkv_bits[:, :hq], qkv_bits[:, hq:hq + hkv], qkv_bits[:, hq + hkv:]
+
+
+def _check_full(qkv, dy, hq, hkv, scale, causal, cu, tag):
+    r = Run(qkv, hq, hkv, scale, causal, cu)
+    o, lse = r.fwd()
+    q, k, v = _split(qkv, hq, hkv)
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, scale, causal, cu)
+    assert_close(tag + " O", oracle.bf16_to_f64(o), o_ref, FWD_MAX_ABS, FWD_REL)
+    assert_close(tag + " LSE", lse.astype(np.float64), lse_ref, LSE_MAX_ABS, 1.0)
+    dq, dk, dv = r.bwd(dy)
+    dq_ref, dk_ref, dv_ref = oracle.attn_bwd(q, k, v, dy, scale, causal, cu)
+    assert_close(tag + " dQ", oracle.bf16_to_f64(dq), dq_ref, GRAD_MAX_ABS, GRAD_REL)
+    assert_close(tag + " dK", oracle.bf16_to_f64(dk), dk_ref, GRAD_MAX_ABS, GRAD_REL)
+    assert_close(tag + " dV", oracle.bf16_to_f64(dv), dv_ref, GRAD_MAX_ABS, GRAD_REL)
+    return r
+
+
+SMALL = [
+    # N, hq, hkv, d, causal, cu, sigma
+    (256, 2, 1, 64, True, None, 1.0),
+    (1, 2, 1, 64, True, None, 1.0),
+    (33, 4, 2, 128, True, None, 0.5),
+    (300, 4, 2, 128, True, None, 0.5),
+    (1000, 8, 2, 128, True, None, 0.5),
+    (517, 4, 4, 64, False, None, 1.0),
+    (777, 3, 1, 128, True, None, 0.5),
+    (640, 4, 2, 128, True, [0, 1, 2, 100, 101, 350, 640], 0.5),
+    (700, 2, 1, 64, False, [0, 64, 65, 300, 700], 1.0),
+    (1536, 8, 2, 128, True, None, 0.5),
+]
+
+
+@pytest.mark.parametrize("N,hq,hkv,d,causal,cu,sigma", SMALL)
+def test_attention_small_full_oracle(N, hq, hkv, d, causal, cu, sigma):
+    print("attn N=%d hq=%d hkv=%d d=%d causal=%d docs=%s" % (N, hq, hkv, d, causal, cu), flush=True)
+    qkv = workloads.normal_bf16((N, hq + 2 * hkv, d), seed=N * 7 + hq, sigma=sigma)
+    dy = workloads.normal_bf16((N, hq, d), seed=N * 11 + d)
+    cu_a = None if cu is None else np.array(cu, dtype=np.int32)
+    _check_full(qkv, dy, hq, hkv, 1.0 / np.sqrt(d), causal, cu_a, "N=%d" % N)
+
+
+def test_tiny_workload_full_ulysses_layer():
+    """The whole tiny layer on the GPU: seq->head pack on both simulated ranks,
+    exchange, attention fwd/bwd per rank, head->seq unpack; compared with the
+    oracle's full-head attention in sequence layout."""
+    w = workloads.WORKLOADS["tiny"]
+    X = workloads.gen_x(w, range(w.Ht))
+    dY = workloads.gen_dy(w, range(w.Hq))
+    Q, K, V = X[:, :w.Hq], X[:, w.Hq:w.Hq + w.Hkv], X[:, w.Hq + w.Hkv:]
+    o_ref, lse_ref = oracle.attn_fwd(Q, K, V, w.scale, True)
+    dq_ref, dk_ref, dv_ref = oracle.attn_bwd(Q, K, V, dY, w.scale, True)
+
+    sends, dsends = [], []
+    for s in range(w.P):
+        xs = dev(X[s * w.n:(s + 1) * w.n])
+        out = sentinel((w.P, w.n, w.ht, w.d))
+        uly.ulysses_seq_to_head(xs, out, w.P, w.segments)
+        sends.append(out)
+        ds = dev(dY[s * w.n:(s + 1) * w.n])
+        dout = sentinel((w.P, w.n, w.hq, w.d))
+        uly.ulysses_seq_to_head(ds, dout, w.P, [w.Hq])
+        dsends.append(dout)
+    o_chunks, g_chunks = [], []
+    for r in range(w.P):
+        recv = torch.stack([sends[s][r] for s in range(w.P)]).reshape(w.N, w.ht, w.d)
+        drecv = torch.stack([dsends[s][r] for s in range(w.P)]).reshape(w.N, w.hq, w.d)
+        q, k, v = recv[:, :w.hq], recv[:, w.hq:w.hq + w.hkv], recv[:, w.hq + w.hkv:]
+        o = sentinel((w.N, w.hq, w.d))
+        lse = torch.empty((w.hq, w.N), dtype=torch.float32, device="cuda")
+        uly.attn_fwd(q, k, v, o, lse, w.scale, True)
+        assert_close("tiny rank%d LSE" % r, lse.cpu().numpy().astype(np.float64),
+                     lse_ref[r * w.hq:(r + 1) * w.hq], LSE_MAX_ABS, 1.0)
+        dqkv = sentinel((w.N, w.ht, w.d))
+        ws = torch.empty(uly.attn_bwd_workspace_bytes(w.N, w.hq, w.hkv, w.d), dtype=torch.uint8, device="cuda")
+        uly.attn_bwd(q, k, v, o, lse, drecv, dqkv[:, :w.hq], dqkv[:, w.hq:w.hq + w.hkv], dqkv[:, w.hq + w.hkv:],
+                     w.scale, True, ws)
+        o_chunks.append(o.reshape(w.P, w.n, w.hq, w.d))
+        g_chunks.append(dqkv.reshape(w.P, w.n, w.ht, w.d))
+    o_seq, g_seq = [], []
+    for s in range(w.P):
+        o_recv = torch.stack([o_chunks[r][s] for r in range(w.P)])     # chunk r from rank r
+        g_recv = torch.stack([g_chunks[r][s] for r in range(w.P)])
+        o_out = sentinel((w.n, w.Hq, w.d))
+        uly.ulysses_head_to_seq(o_recv.contiguous(), o_out, w.P, [w.Hq])
+        g_out = sentinel((w.n, w.Ht, w.d))
+        uly.ulysses_head_to_seq(g_recv.contiguous(), g_out, w.P, w.segments)
+        o_seq.append(f64(o_out))
+        g_seq.append(f64(g_out))
+    O = np.concatenate(o_seq)
+    G = np.concatenate(g_seq)
+    assert_close("tiny layer O", O, o_ref, FWD_MAX_ABS, FWD_REL)
+    assert_close("tiny layer dQ", G[:, :w.Hq], dq_ref, GRAD_MAX_ABS, GRAD_REL)
+    assert_close("tiny layer dK", G[:, w.Hq:w.Hq + w.Hkv], dk_ref, GRAD_MAX_ABS, GRAD_REL)
+    assert_close("tiny layer dV", G[:, w.Hq + w.Hkv:], dv_ref, GRAD_MAX_ABS, GRAD_REL)
+
+
+def _sample_rows(N, n_local, count, seed):
+    rng = np.random.default_rng(seed)
+    must = [0, 1, 63, 64, N - 1, N - 2]
+    for s in range(1, N // n_local):
+        must += [s * n_local - 1, s * n_local, s * n_local + 1]
+    rows = set(x for x in must if 0 <= x < N)
+    rows.update(int(x) for x in rng.integers(0, N, size=count))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", ["8k", "64k", "varlen", "256k"])
+def test_workload_head_shard_sampled(name):
+    """Rank 0's head shard at the workload's full size, in the launch shape the
+    benchmark times; oracle on sampled query rows (O, LSE, dQ) and on the
+    last 128 keys (dK, dV)."""
+    w = workloads.WORKLOADS[name]
+    print("workload %s N=%d hq=%d hkv=%d" % (name, w.N, w.hq, w.hkv), flush=True)
+    qkv = workloads.gen_head_shard(w, 0)
+    dy = workloads.gen_dy_head_shard(w, 0)
+    cu = workloads.cu_seqlens(w) if w.varlen else None
+    r = Run(qkv, w.hq, w.hkv, w.scale, True, cu)
+    o, lse = r.fwd()
+    dq, dk, dv = r.bwd(dy)
+    q, k, v = _split(qkv, w.hq, w.hkv)
+    rows = _sample_rows(w.N, w.n, 96 if name == "256k" else 160, seed=len(name))
+    if cu is not None:
+        rows = np.unique(np.concatenate([rows, cu[:-1], cu[1:] - 1]))
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, w.scale, True, cu, rows=rows)
+    assert_close(name + " O[rows]", oracle.bf16_to_f64(o[rows]), o_ref, FWD_MAX_ABS, FWD_REL)
+    assert_close(name + " LSE[rows]", lse[:, rows].astype(np.float64), lse_ref, LSE_MAX_ABS, 1.0)
+    klo = w.N - 128
+    dq_ref, dk_ref, dv_ref = oracle.attn_bwd(q, k, v, dy, w.scale, True, cu, rows=rows, key_lo=klo)
+    assert_close(name + " dQ[rows]", oracle.bf16_to_f64(dq[rows]), dq_ref, GRAD_MAX_ABS, GRAD_REL)
+    assert_close(name + " dK[tail]", oracle.bf16_to_f64(dk[klo:]), dk_ref, GRAD_MAX_ABS, GRAD_REL)
+    assert_close(name + " dV[tail]", oracle.bf16_to_f64(dv[klo:]), dv_ref, GRAD_MAX_ABS, GRAD_REL)
+    for t, nm in ((o, "O"), (dq, "dQ"), (dk, "dK"), (dv, "dV")):
+        assert np.all(np.isfinite(oracle.bf16_to_f64(t))), nm + " has unwritten/non-finite elements"
+
+
+def test_q_zero_closed_form_full_size():
+    """Q = 0 at 64K: o_i = mean(v_0..v_i), LSE_i = ln(i+1) for every row, and
+    dK = 0 exactly (checked over all N rows via prefix sums)."""
+    w = workloads.WORKLOADS["64k"]
+    qkv = workloads.gen_head_shard(w, 0)
+    qkv[:, :w.hq] = 0
+    dy = workloads.gen_dy_head_shard(w, 0)
+    r = Run(qkv, w.hq, w.hkv, w.scale, True)
+    o, lse = r.fwd()
+    v = oracle.bf16_to_f64(qkv[:, w.hq + w.hkv:])
+    mean = np.cumsum(v, axis=0) / np.arange(1, w.N + 1)[:, None, None]
+    G = w.hq // w.hkv
+    for h in range(w.hq):
+        assert_close("Q=0 O head %d" % h, oracle.bf16_to_f64(o[:, h]), mean[:, h // G], FWD_MAX_ABS, FWD_REL)
+    assert_close("Q=0 LSE", lse.astype(np.float64), np.broadcast_to(np.log(np.arange(1, w.N + 1)), lse.shape),
+                 LSE_MAX_ABS, 1.0)
+    dq, dk, dv = r.bwd(dy)
+    assert np.all(oracle.bf16_to_f64(dk) == 0.0)
+
+
+def test_determinism_and_causality():
+    N, hq, hkv, d = 1200, 4, 2, 128
+    qkv = workloads.normal_bf16((N, hq + 2 * hkv, d), seed=77, sigma=0.5)
+    dy = workloads.normal_bf16((N, hq, d), seed=78)
+    r1 = Run(qkv, hq, hkv, 1 / np.sqrt(d))
+    o1, l1 = r1.fwd()
+    g1 = r1.bwd(dy)
+    r2 = Run(qkv, hq, hkv, 1 / np.sqrt(d))
+    o2, l2 = r2.fwd()
+    g2 = r2.bwd(dy)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    for a, b in zip(g1, g2):
+        assert np.array_equal(a, b)
+    # perturb every token after i: rows <= i of O and LSE must not change (bits)
+    i = 517
+    qkv2 = qkv.copy()
+    qkv2[i + 1:] = workloads.normal_bf16(qkv2[i + 1:].shape, seed=79, sigma=0.5)
+    o3, l3 = Run(qkv2, hq, hkv, 1 / np.sqrt(d)).fwd()
+    assert np.array_equal(o3[:i + 1], o1[:i + 1]) and np.array_equal(l3[:, :i + 1], l1[:, :i + 1])
+
+
+def test_head_shards_concatenate_to_full_heads_bitexact():
+    """Ulysses composition on the GPU: per-rank head-shard runs, side by side,
+    equal the full-head run bit for bit (heads are independent)."""
+    w = workloads.WORKLOADS["tiny"]
+    X = workloads.gen_x(w, range(w.Ht))
+    dY = workloads.gen_dy(w, range(w.Hq))
+    full = Run(X, w.Hq, w.Hkv, w.scale)
+    of, lf = full.fwd()
+    dqf, dkf, dvf = full.bwd(dY)
+    for r in range(w.P):
+        sh = Run(workloads.gen_head_shard(w, r), w.hq, w.hkv, w.scale)
+        o, l = sh.fwd()
+        dq, dk, dv = sh.bwd(workloads.gen_dy_head_shard(w, r))
+        hs, ks = slice(r * w.hq, (r + 1) * w.hq), slice(r * w.hkv, (r + 1) * w.hkv)
+        assert np.array_equal(o, of[:, hs]) and np.array_equal(l, lf[hs])
+        assert np.array_equal(dq, dqf[:, hs]) and np.array_equal(dk, dkf[:, ks]) and np.array_equal(dv, dvf[:, ks])
+
+
+def test_varlen_single_document_equals_dense_and_per_doc_runs():
+    N, hq, hkv, d = 900, 4, 2, 128
+    qkv = workloads.normal_bf16((N, hq + 2 * hkv, d), seed=91, sigma=0.5)
+    dy = workloads.normal_bf16((N, hq, d), seed=92)
+    dense = Run(qkv, hq, hkv, 1 / np.sqrt(d))
+    od, ld = dense.fwd()
+    gd = dense.bwd(dy)
+    one = Run(qkv, hq, hkv, 1 / np.sqrt(d), cu=np.array([0, N], dtype=np.int32))
+    o1, l1 = one.fwd()
+    g1 = one.bwd(dy)
+    assert np.array_equal(od, o1) and np.array_equal(ld, l1)
+    for a, b in zip(gd, g1):
+        assert np.array_equal(a, b)
+    cu = np.array([0, 130, 131, 500, 900], dtype=np.int32)
+    packed = Run(qkv, hq, hkv, 1 / np.sqrt(d), cu=cu)
+    op, lp = packed.fwd()
+    gp = packed.bwd(dy)
+    for a, b in zip(cu[:-1], cu[1:]):
+        doc = Run(np.ascontiguousarray(qkv[a:b]), hq, hkv, 1 / np.sqrt(d))
+        o_doc, l_doc = doc.fwd()
+        g_doc = doc.bwd(np.ascontiguousarray(dy[a:b]))
+        assert_close("doc O", oracle.bf16_to_f64(op[a:b]), oracle.bf16_to_f64(o_doc), 1e-2, 1e-2)
+        assert np.max(np.abs(lp[:, a:b] - l_doc)) < 1e-4
+        for x, y in zip(gp, g_doc):
+            assert_close("doc grad", oracle.bf16_to_f64(x[a:b]), oracle.bf16_to_f64(y), 3e-2, 3e-2)
+
+
+def test_attention_argument_errors():
+    q = torch.zeros((64, 4, 128), dtype=torch.int16, device="cuda")
+    kv = torch.zeros((64, 3, 128), dtype=torch.int16, device="cuda")
+    o = sentinel((64, 4, 128))
+    lse = torch.zeros((4, 64), dtype=torch.float32, device="cuda")
+    with pytest.raises(uly.UlyssesError) as e:
+        uly.attn_fwd(q, kv, kv, o, lse, 0.1)                  # 4 % 3 != 0
+    assert e.value.name == "ULY_E_GQA"
+    q96 = torch.zeros((64, 4, 96), dtype=torch.int16, device="cuda")
+    with pytest.raises(uly.UlyssesError) as e:
+        uly.attn_fwd(q96, q96[:, :2], q96[:, :2], q96.clone(), lse, 0.1)
+    assert e.value.name == "ULY_E_HEADDIM"
+    with pytest.raises(uly.UlyssesError) as e:
+        uly.attn_fwd(q, q[:, :2], q[:, :2], q, lse, 0.1)      # o aliases q
+    assert e.value.name == "ULY_E_ALIAS"
+    torch.cuda.synchronize()
+    assert np.all(host(o) == 0xFFFF)
