@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark of one Ulysses rank's hot path on one MI355X.
+
+One step is one pass over every step of the path for one simulated rank, on
+seeded synthetic inputs already resident in HBM:
+  seq->head pack of fused QKV -> attention forward -> head->seq unpack of O
+  -> seq->head pack of dO -> attention backward (D + dQ, then dK/dV)
+  -> head->seq unpack of the fused dQKV.
+The all-to-all between the packs and the attention (a re-indexing of buffers
+across ranks) is not a kernel of this rank and is not timed: the attention
+reads the rank's head shard generated directly.
+
+Prints ONE JSON line on stdout. Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd+bwd TFLOP/s (% bf16 MFMA peak) at 64K head-shard; swap GB/s"
+BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def unmasked_pairs(w, cu):
+    """U: (query, key) pairs the mask allows, per query head."""
+    if cu is None:
+        return w.N * (w.N + 1) // 2
+    lens = [int(b - a) for a, b in zip(cu[:-1], cu[1:])]
+    return sum(L * (L + 1) // 2 for L in lens)
+
+
+def cpu_baseline(w, tokens: int):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    causal fwd + bwd (all dQ rows, all dK/dV keys) over the first `tokens`
+    tokens of rank 0's head shard, all its heads. Counted like the GPU:
+    14 * d flop per unmasked (query, key) pair per query head."""
+    import numpy as np
+
+    import oracle
+    import workloads
+    qkv = workloads.gen_x(w, workloads.rank_heads(w, 0), 0, tokens)
+    dy = workloads.gen_dy(w, [c for c in range(w.hq)], 0, tokens)
+    q, k, v = qkv[:, :w.hq], qkv[:, w.hq:w.hq + w.hkv], qkv[:, w.hq + w.hkv:]
+    t0 = time.perf_counter()
+    oracle.attn_fwd(q, k, v, w.scale, True)
+    oracle.attn_bwd(q, k, v, dy, w.scale, True)
+    dt = time.perf_counter() - t0
+    U = tokens * (tokens + 1) // 2
+    flops = 14.0 * w.d * U * w.hq
+    del np
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": "fp64 oracle causal attention fwd+bwd over the first %d of %d tokens of the head shard "
+                  "(%d q / %d kv heads, d=%d); %.1f s" % (tokens, w.N, w.hq, w.hkv, w.d, dt),
+        "seconds": dt,
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="64k", choices=["tiny", "8k", "64k", "varlen", "256k"])
+    ap.add_argument("--cpu-tokens", type=int, default=3072,
+                    help="tokens of the oracle's CPU-baseline sample (0 = skip)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU's share of the Ulysses path; runs on more than one GPU "
+              "are not part of this build (requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import long_context_attention_ulysses_amd as uly
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = workloads.WORKLOADS[args.workload]
+    cu = workloads.cu_seqlens(w) if w.varlen else None
+    log("workload %s: N=%d P=%d hq=%d hkv=%d d=%d" % (w.name, w.N, w.P, w.hq, w.hkv, w.d))
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+    t_gen = time.perf_counter()
+    x_seq = dev(workloads.gen_seq_shard(w, 0))            # [n, Ht, d]  this rank's tokens
+    recv = dev(workloads.gen_head_shard(w, 0))            # [N, ht, d]  its head shard
+    dy_seq = dev(workloads.gen_dy_seq_shard(w, 0))        # [n, Hq, d]
+    dy_head = dev(workloads.gen_dy_head_shard(w, 0))      # [N, hq, d]
+    log("inputs generated in %.1f s" % (time.perf_counter() - t_gen))
+    cu_dev = None if cu is None else torch.tensor(cu, dtype=torch.int32, device="cuda")
+
+    n, P, hq, hkv, ht, d = w.n, w.P, w.hq, w.hkv, w.ht, w.d
+    send = torch.empty((P, n, ht, d), dtype=torch.int16, device="cuda")
+    q, k, v = recv[:, :hq], recv[:, hq:hq + hkv], recv[:, hq + hkv:]
+    o = torch.empty((w.N, hq, d), dtype=torch.int16, device="cuda")
+    lse = torch.empty((hq, w.N), dtype=torch.float32, device="cuda")
+    o_seq = torch.empty((n, w.Hq, d), dtype=torch.int16, device="cuda")
+    dsend = torch.empty((P, n, hq, d), dtype=torch.int16, device="cuda")
+    dqkv = torch.empty((w.N, ht, d), dtype=torch.int16, device="cuda")
+    dq, dk, dv = dqkv[:, :hq], dqkv[:, hq:hq + hkv], dqkv[:, hq + hkv:]
+    dqkv_seq = torch.empty((n, w.Ht, d), dtype=torch.int16, device="cuda")
+    ws = torch.empty(uly.attn_bwd_workspace_bytes(w.N, hq, hkv, d, 1 if cu is None else len(cu) - 1),
+                     dtype=torch.uint8, device="cuda")
+    o_chunks = o.view(P, n, hq, d)          # O's P destination chunks (token blocks)
+    g_chunks = dqkv.view(P, n, ht, d)
+
+    names = ["a1_pack_qkv", "a3_attn_fwd", "a5_unpack_o", "a6_pack_do", "a7a9_attn_bwd_dq",
+             "a8_attn_bwd_dkdv", "a10_unpack_dqkv"]
+    launches = [
+        lambda: uly.ulysses_seq_to_head(x_seq, send, P, w.segments),
+        lambda: uly.attn_fwd(q, k, v, o, lse, w.scale, True, cu_dev, None),
+        lambda: uly.ulysses_head_to_seq(o_chunks, o_seq, P, [w.Hq]),
+        lambda: uly.ulysses_seq_to_head(dy_seq, dsend, P, [w.Hq]),
+        lambda: uly.attn_bwd_dq(q, k, v, o, lse, dy_head, dq, w.scale, True, ws, cu_dev),
+        lambda: uly.attn_bwd_dkdv(q, k, v, lse, dy_head, dk, dv, w.scale, True, ws, cu_dev),
+        lambda: uly.ulysses_head_to_seq(g_chunks, dqkv_seq, P, w.segments),
+    ]
+    swap_bytes = {
+        "a1_pack_qkv": 2 * n * w.Ht * d * 2,
+        "a5_unpack_o": 2 * n * w.Hq * d * 2,
+        "a6_pack_do": 2 * n * w.Hq * d * 2,
+        "a10_unpack_dqkv": 2 * n * w.Ht * d * 2,
+    }
+    U = unmasked_pairs(w, cu)
+    flops = {
+        "a3_attn_fwd": 4.0 * d * U * hq,
+        "a7a9_attn_bwd_dq": 2.0 * d * U * hq,      # dQ; its recompute of S and dP is not counted
+        "a8_attn_bwd_dkdv": 8.0 * d * U * hq,      # S recompute, dP, dV, dK
+    }
+    total_flops = 14.0 * d * U * hq
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+              for _ in range(args.steps)]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        for i, f in enumerate(launches):
+            f()
+            if ev is not None:
+                ev[i + 1].record()
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log("warmup step %d done" % (i + 1))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    log("timed %d steps: %.3f ms/step" % (args.steps, ms_per_step))
+
+    kern_ms = {nm: float(np.mean([events[s][i].elapsed_time(events[s][i + 1]) for s in range(args.steps)]))
+               for i, nm in enumerate(names)}
+    attn_ms = kern_ms["a3_attn_fwd"] + kern_ms["a7a9_attn_bwd_dq"] + kern_ms["a8_attn_bwd_dkdv"]
+    swap_gbps = {nm: swap_bytes[nm] / (kern_ms[nm] * 1e-3) / 1e9 for nm in swap_bytes}
+    dom = max(flops, key=lambda nm: kern_ms[nm])
+    achieved = flops[dom] / (kern_ms[dom] * 1e-3) / 1e12
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "Qwen3-4B-shaped SP=%d head shard, %s: N=%d tokens, %d q / %d kv heads, d=%d, causal%s"
+                        % (P, w.name, w.N, hq, hkv, d, ", packed docs" if cu is not None else ""),
+            "N": w.N, "P": P, "hq": hq, "hkv": hkv, "d": d, "seq_shard": [n, w.Ht, d],
+            "n_docs": None if cu is None else len(cu) - 1,
+        },
+        "roofline": {
+            "kernel": dom,
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+        },
+        "attn_tflops": round(total_flops / (attn_ms * 1e-3) / 1e12, 2),
+        "attn_frac_peak": round(total_flops / (attn_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "value_frac_peak": round(value / BF16_PEAK_TFLOPS, 4),
+        "tokens_per_s": round(w.N / (attn_ms * 1e-3), 1),
+        "kernel_ms": {k_: round(v_, 4) for k_, v_ in kern_ms.items()},
+        "kernel_tflops": {k_: round(flops[k_] / (kern_ms[k_] * 1e-3) / 1e12, 2) for k_ in flops},
+        "swap_gbps": {k_: round(v_, 1) for k_, v_ in swap_gbps.items()},
+        "swap_frac_hbm": {k_: round(v_ / HBM_PEAK_GBPS, 4) for k_, v_ in swap_gbps.items()},
+        "counted_flop_per_step": total_flops,
+        "unmasked_pairs_per_head": U,
+    }
+    if args.cpu_tokens > 0:
+        log("cpu baseline: oracle on %d tokens ..." % args.cpu_tokens)
+        result["cpu_baseline"] = cpu_baseline(w, min(args.cpu_tokens, w.N))
+        log("cpu baseline done in %.1f s" % result["cpu_baseline"]["seconds"])
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

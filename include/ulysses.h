@@ -182,6 +182,31 @@ int attn_bwd_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
                     float scale, int32_t causal, const int32_t *cu_seqlens, int32_t n_seqs,
                     int32_t max_seqlen, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * The two steps of attn_bwd as separate calls, for callers that schedule them
+ * on their own (e.g. to overlap the second with other work). attn_bwd is
+ * exactly attn_bwd_dq followed by attn_bwd_dkdv on the same stream.
+ *
+ * attn_bwd_dq: D = rowsum(dout * o) into ws (float32 [hq][N]) and dq.
+ * attn_bwd_dkdv: dk and dv, reading D from ws as left by attn_bwd_dq with the
+ *   same arguments (ws must not be modified in between).
+ * cu_seqlens: device table as in attn_fwd_varlen, or NULL for one document
+ * (n_seqs is then ignored). Errors as attn_bwd.
+ */
+int attn_bwd_dq(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *o,
+                const float *lse, const uint16_t *dout, uint16_t *dq, int64_t N, int32_t hq,
+                int32_t hkv, int32_t d, int64_t q_stride, int64_t k_stride, int64_t v_stride,
+                int64_t o_stride, int64_t do_stride, int64_t dq_stride, float scale,
+                int32_t causal, const int32_t *cu_seqlens, int32_t n_seqs, void *ws,
+                size_t ws_bytes, hipStream_t stream);
+
+int attn_bwd_dkdv(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *lse,
+                  const uint16_t *dout, uint16_t *dk, uint16_t *dv, int64_t N, int32_t hq,
+                  int32_t hkv, int32_t d, int64_t q_stride, int64_t k_stride, int64_t v_stride,
+                  int64_t do_stride, int64_t dk_stride, int64_t dv_stride, float scale,
+                  int32_t causal, const int32_t *cu_seqlens, int32_t n_seqs, const void *ws,
+                  size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

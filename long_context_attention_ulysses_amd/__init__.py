@@ -11,6 +11,8 @@ from ._lib import (  # noqa: F401
     CODE,
     UlyssesError,
     attn_bwd,
+    attn_bwd_dkdv,
+    attn_bwd_dq,
     attn_bwd_workspace_bytes,
     attn_fwd,
     raw,

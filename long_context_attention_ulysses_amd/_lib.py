@@ -54,6 +54,10 @@ _SIGS = {
     "attn_bwd": ([_p] * 9 + [_i64, _i32, _i32, _i32] + [_i64] * 8 + [_f32, _i32, _p, _sz, _p], ctypes.c_int),
     "attn_bwd_varlen": ([_p] * 9 + [_i64, _i32, _i32, _i32] + [_i64] * 8 + [_f32, _i32, _p, _i32, _i32, _p, _sz,
                                                                           _p], ctypes.c_int),
+    "attn_bwd_dq": ([_p] * 7 + [_i64, _i32, _i32, _i32] + [_i64] * 6 + [_f32, _i32, _p, _i32, _p, _sz, _p],
+                    ctypes.c_int),
+    "attn_bwd_dkdv": ([_p] * 7 + [_i64, _i32, _i32, _i32] + [_i64] * 6 + [_f32, _i32, _p, _i32, _p, _sz, _p],
+                      ctypes.c_int),
 }
 for _name, (_args, _res) in _SIGS.items():
     _f = getattr(_L, _name)
@@ -171,3 +175,29 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, scale: float, causal: bool = Tru
     else:
         _check(_L.attn_bwd_varlen(*args, _ptr(cu_seqlens), n_seqs, int(max_seqlen or N), _ptr(ws), ws_bytes,
                                   _stream(stream)), "attn_bwd_varlen")
+
+
+def attn_bwd_dq(q, k, v, o, lse, dout, dq, scale: float, causal: bool = True, ws=None, cu_seqlens=None,
+                stream=None) -> None:
+    """First step of attn_bwd: D = rowsum(dout * o) into ws, and dq."""
+    N, hq, d = q.shape
+    hkv = k.shape[1]
+    n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    _check(_L.attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), N, hq, hkv, d,
+                          _tok_stride(q, hq, d), _tok_stride(k, hkv, d), _tok_stride(v, hkv, d),
+                          _tok_stride(o, hq, d), _tok_stride(dout, hq, d), _tok_stride(dq, hq, d), float(scale),
+                          int(bool(causal)), _ptr(cu_seqlens), n_seqs, _ptr(ws), ws.numel() * ws.element_size(),
+                          _stream(stream)), "attn_bwd_dq")
+
+
+def attn_bwd_dkdv(q, k, v, lse, dout, dk, dv, scale: float, causal: bool = True, ws=None, cu_seqlens=None,
+                  stream=None) -> None:
+    """Second step of attn_bwd: dk and dv, reading D from ws (left by attn_bwd_dq)."""
+    N, hq, d = q.shape
+    hkv = k.shape[1]
+    n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    _check(_L.attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(dk), _ptr(dv), N, hq, hkv, d,
+                            _tok_stride(q, hq, d), _tok_stride(k, hkv, d), _tok_stride(v, hkv, d),
+                            _tok_stride(dout, hq, d), _tok_stride(dk, hkv, d), _tok_stride(dv, hkv, d),
+                            float(scale), int(bool(causal)), _ptr(cu_seqlens), n_seqs, _ptr(ws),
+                            ws.numel() * ws.element_size(), _stream(stream)), "attn_bwd_dkdv")

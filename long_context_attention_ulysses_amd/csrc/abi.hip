@@ -117,17 +117,18 @@ int attn_bwd_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
                   uint16_t *dv, int64_t N, int32_t hq, int32_t hkv, int32_t d, int64_t qs,
                   int64_t ks, int64_t vs, int64_t os, int64_t dos, int64_t dqs, int64_t dks,
                   int64_t dvs, float scale, int32_t causal, const int32_t *cu, int32_t n_seqs,
-                  void *ws, size_t ws_bytes, hipStream_t stream) {
+                  const void *ws, size_t ws_bytes, int parts, hipStream_t stream) {
   int rc = check_attn_common(q, k, v, N, hq, hkv, d, qs, ks, vs, scale);
   if (rc) return rc;
-  if (!o || !lse || !dout) return ULY_E_NULL;
+  const bool want_dq = parts & 1, want_dkv = parts & 2;
+  if (!lse || !dout || (want_dq && !o)) return ULY_E_NULL;
   const int64_t wq = (int64_t)hq * d, wk = (int64_t)hkv * d;
-  if (os < wq || dos < wq) return ULY_E_STRIDE;
-  if (os % 8 || dos % 8) return ULY_E_ALIGN;
-  if (!aligned16(o) || !aligned16(dout)) return ULY_E_ALIGN;
-  if ((rc = check_out(dq, N, dqs, wq))) return rc;
-  if ((rc = check_out(dk, N, dks, wk))) return rc;
-  if ((rc = check_out(dv, N, dvs, wk))) return rc;
+  if (dos < wq || (want_dq && os < wq)) return ULY_E_STRIDE;
+  if (dos % 8 || (want_dq && os % 8)) return ULY_E_ALIGN;
+  if (!aligned16(dout) || (want_dq && !aligned16(o))) return ULY_E_ALIGN;
+  if (want_dq && (rc = check_out(dq, N, dqs, wq))) return rc;
+  if (want_dkv && (rc = check_out(dk, N, dks, wk))) return rc;
+  if (want_dkv && (rc = check_out(dv, N, dvs, wk))) return rc;
   if (!ws) return ULY_E_WORKSPACE;
   if (ws_bytes < attn_bwd_workspace_bytes(N, hq, hkv, d, n_seqs)) return ULY_E_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return ULY_E_WORKSPACE;
@@ -137,15 +138,19 @@ int attn_bwd_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
     const void *p;
     size_t n;
   };
-  const R ins[] = {{q, span_bytes(N, qs, wq)},     {k, span_bytes(N, ks, wk)},
-                   {v, span_bytes(N, vs, wk)},     {o, span_bytes(N, os, wq)},
-                   {dout, span_bytes(N, dos, wq)}, {lse, (size_t)N * hq * 4},
+  const R ins[] = {{q, span_bytes(N, qs, wq)},
+                   {k, span_bytes(N, ks, wk)},
+                   {v, span_bytes(N, vs, wk)},
+                   {o, want_dq ? span_bytes(N, os, wq) : 0},
+                   {dout, span_bytes(N, dos, wq)},
+                   {lse, (size_t)N * hq * 4},
                    {ws, (size_t)N * hq * 4}};
-  const R outs[] = {{dq, span_bytes(N, dqs, wq)}, {dk, span_bytes(N, dks, wk)},
-                    {dv, span_bytes(N, dvs, wk)}};
+  const R outs[] = {{dq, want_dq ? span_bytes(N, dqs, wq) : 0},
+                    {dk, want_dkv ? span_bytes(N, dks, wk) : 0},
+                    {dv, want_dkv ? span_bytes(N, dvs, wk) : 0}};
   for (const R &x : outs)
     for (const R &y : ins)
-      if (overlaps(x.p, x.n, y.p, y.n)) return ULY_E_ALIAS;
+      if (x.n && y.n && overlaps(x.p, x.n, y.p, y.n)) return ULY_E_ALIAS;
   AttnShape s;
   s.N = N;
   s.hq = hq;
@@ -158,7 +163,7 @@ int attn_bwd_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
   s.scale = scale;
   s.causal = causal ? 1 : 0;
   s.cu = cu;
-  s.n_seqs = n_seqs;
+  s.n_seqs = cu ? n_seqs : 0;
   AttnBwdPtrs p;
   p.q = q;
   p.k = k;
@@ -173,8 +178,8 @@ int attn_bwd_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
   p.dq_stride = dqs;
   p.dk_stride = dks;
   p.dv_stride = dvs;
-  p.delta = static_cast<float *>(ws);
-  return launch_attn_bwd(s, p, stream);
+  p.delta = static_cast<float *>(const_cast<void *>(ws));
+  return launch_attn_bwd(s, p, parts, stream);
 }
 
 }  // namespace
@@ -270,7 +275,7 @@ int attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint
              size_t ws_bytes, hipStream_t stream) {
   return attn_bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, N, hq, hkv, d, q_stride, k_stride,
                        v_stride, o_stride, do_stride, dq_stride, dk_stride, dv_stride, scale,
-                       causal, nullptr, 0, ws, ws_bytes, stream);
+                       causal, nullptr, 0, ws, ws_bytes, 3, stream);
 }
 
 int attn_bwd_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *o,
@@ -284,7 +289,31 @@ int attn_bwd_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
   if (rc) return rc;
   return attn_bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, N, hq, hkv, d, q_stride, k_stride,
                        v_stride, o_stride, do_stride, dq_stride, dk_stride, dv_stride, scale,
-                       causal, cu_seqlens, n_seqs, ws, ws_bytes, stream);
+                       causal, cu_seqlens, n_seqs, ws, ws_bytes, 3, stream);
+}
+
+int attn_bwd_dq(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *o,
+                const float *lse, const uint16_t *dout, uint16_t *dq, int64_t N, int32_t hq,
+                int32_t hkv, int32_t d, int64_t q_stride, int64_t k_stride, int64_t v_stride,
+                int64_t o_stride, int64_t do_stride, int64_t dq_stride, float scale,
+                int32_t causal, const int32_t *cu_seqlens, int32_t n_seqs, void *ws,
+                size_t ws_bytes, hipStream_t stream) {
+  if (cu_seqlens && (n_seqs <= 0 || n_seqs > N)) return ULY_E_SHAPE;
+  return attn_bwd_impl(q, k, v, o, lse, dout, dq, nullptr, nullptr, N, hq, hkv, d, q_stride,
+                       k_stride, v_stride, o_stride, do_stride, dq_stride, 0, 0, scale, causal,
+                       cu_seqlens, n_seqs, ws, ws_bytes, 1, stream);
+}
+
+int attn_bwd_dkdv(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *lse,
+                  const uint16_t *dout, uint16_t *dk, uint16_t *dv, int64_t N, int32_t hq,
+                  int32_t hkv, int32_t d, int64_t q_stride, int64_t k_stride, int64_t v_stride,
+                  int64_t do_stride, int64_t dk_stride, int64_t dv_stride, float scale,
+                  int32_t causal, const int32_t *cu_seqlens, int32_t n_seqs, const void *ws,
+                  size_t ws_bytes, hipStream_t stream) {
+  if (cu_seqlens && (n_seqs <= 0 || n_seqs > N)) return ULY_E_SHAPE;
+  return attn_bwd_impl(q, k, v, nullptr, lse, dout, nullptr, dk, dv, N, hq, hkv, d, q_stride,
+                       k_stride, v_stride, 0, do_stride, 0, dk_stride, dv_stride, scale, causal,
+                       cu_seqlens, n_seqs, ws, ws_bytes, 2, stream);
 }
 
 }  // extern "C"

@@ -569,7 +569,7 @@ int launch_dkdv_cfg(BwdArgs a, hipStream_t stream) {
 
 }  // namespace
 
-int launch_attn_bwd(const AttnShape &s, const AttnBwdPtrs &p, hipStream_t stream) {
+int launch_attn_bwd(const AttnShape &s, const AttnBwdPtrs &p, int parts, hipStream_t stream) {
   BwdArgs a;
   a.q = p.q;
   a.k = p.k;
@@ -600,19 +600,21 @@ int launch_attn_bwd(const AttnShape &s, const AttnBwdPtrs &p, hipStream_t stream
   a.cu = s.cu;
   a.n_seqs = s.n_seqs;
   const int hpw = (a.G % 4 == 0) ? 4 : (a.G % 2 == 0) ? 2 : 1;
-  int rc;
+  int rc = 0;
   if (s.d == 128) {
-    rc = hpw == 4 ? launch_dq_cfg<128, 4, 1>(a, stream)
-         : hpw == 2 ? launch_dq_cfg<128, 2, 2>(a, stream)
-                    : launch_dq_cfg<128, 1, 4>(a, stream);
+    if (parts & 1)
+      rc = hpw == 4 ? launch_dq_cfg<128, 4, 1>(a, stream)
+           : hpw == 2 ? launch_dq_cfg<128, 2, 2>(a, stream)
+                      : launch_dq_cfg<128, 1, 4>(a, stream);
     if (rc) return rc;
-    return launch_dkdv_cfg<128, 4>(a, stream);
+    return (parts & 2) ? launch_dkdv_cfg<128, 4>(a, stream) : 0;
   }
-  rc = hpw == 4 ? launch_dq_cfg<64, 4, 2>(a, stream)
-       : hpw == 2 ? launch_dq_cfg<64, 2, 4>(a, stream)
-                  : launch_dq_cfg<64, 1, 8>(a, stream);
+  if (parts & 1)
+    rc = hpw == 4 ? launch_dq_cfg<64, 4, 2>(a, stream)
+         : hpw == 2 ? launch_dq_cfg<64, 2, 4>(a, stream)
+                    : launch_dq_cfg<64, 1, 8>(a, stream);
   if (rc) return rc;
-  return launch_dkdv_cfg<64, 4>(a, stream);
+  return (parts & 2) ? launch_dkdv_cfg<64, 4>(a, stream) : 0;
 }
 
 }  // namespace uly

@@ -47,6 +47,10 @@ struct FwdArgs {
   int n_seqs;
 };
 
+// Headroom (log2 units) the running max may lag the true max by; see the
+// softmax step of the kernel.
+constexpr float kMaxSlack = 8.f;
+
 template <int D, int NQB, int HPW, int RB>
 struct FwdCfg {
   static constexpr int NW = HPW * RB;
@@ -264,10 +268,23 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[nb][kb][i]);
         mx = fmaxf(mx, xor32(mx));
-        const float m_new = fmaxf(m_run[nb], mx * a.c);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run[nb] - m_use);
-        m_run[nb] = m_new;
+        // The running max m only moves when this tile's max exceeds it by
+        // more than kMaxSlack (log2 units), so p = exp2(s*c - m) stays below
+        // 2^kMaxSlack; O and l are rescaled only when some lane of the wave
+        // moves its max. The result is exact either way (O / l and
+        // m + log2 l do not depend on which m was used).
+        const float m_cand = mx * a.c;
+        const bool grow = m_cand > m_run[nb] + kMaxSlack;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+          const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[nb] - m_cand) : 1.f;
+          m_run[nb] = grow ? m_cand : m_run[nb];
+          l_run[nb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc_o[nb][db][i] *= alpha;
+        }
+        const float m_use = (m_run[nb] == -INFINITY) ? 0.f : m_run[nb];
         float rs = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -277,11 +294,7 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_fwd_kernel(FwdArgs a) {
             s[nb][kb][i] = p;
             rs += p;
           }
-        l_run[nb] = l_run[nb] * alpha + rs;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc_o[nb][db][i] *= alpha;
+        l_run[nb] += rs;
 #pragma unroll
         for (int j = 0; j < C::JS; ++j) {
           const f32x16 &sv = s[nb][j >> 1];

@@ -43,14 +43,14 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t x) {
   return __uint_as_float(((uint32_t)x) << 16);
 }
 
-// fp32 -> bf16, round to nearest even (inputs are finite here).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
+// Two fp32 -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32;
+// `lo` lands in the low half.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 }  // namespace uly

@@ -40,6 +40,7 @@ struct AttnBwdPtrs {
   float *delta;  // workspace: D = rowsum(dO * O), [hq][N] float32
 };
 
-int launch_attn_bwd(const AttnShape &s, const AttnBwdPtrs &p, hipStream_t stream);
+// parts: 1 = D and dQ, 2 = dK and dV (reads D), 3 = both in that order.
+int launch_attn_bwd(const AttnShape &s, const AttnBwdPtrs &p, int parts, hipStream_t stream);
 
 }  // namespace uly

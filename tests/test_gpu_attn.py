@@ -293,3 +293,22 @@ def test_attention_argument_errors():
     assert e.value.name == "ULY_E_ALIAS"
     torch.cuda.synchronize()
     assert np.all(host(o) == 0xFFFF)
+
+
+def test_split_backward_equals_attn_bwd():
+    """attn_bwd_dq then attn_bwd_dkdv gives attn_bwd's bits."""
+    N, hq, hkv, d = 700, 8, 2, 128
+    qkv = workloads.normal_bf16((N, hq + 2 * hkv, d), seed=101, sigma=0.5)
+    dy = workloads.normal_bf16((N, hq, d), seed=102)
+    for cu in (None, np.array([0, 100, 101, 700], dtype=np.int32)):
+        r = Run(qkv, hq, hkv, 1 / np.sqrt(d), cu=cu)
+        r.fwd()
+        ref = r.bwd(dy)
+        dq = sentinel((N, hq, d))
+        dkv = sentinel((N, 2 * hkv, d))
+        ws = torch.empty(uly.attn_bwd_workspace_bytes(N, hq, hkv, d), dtype=torch.uint8, device="cuda")
+        uly.attn_bwd_dq(r.q, r.k, r.v, r.o, r.lse, r.dy, dq, r.scale, True, ws, r.cu_dev)
+        uly.attn_bwd_dkdv(r.q, r.k, r.v, r.lse, r.dy, dkv[:, :hkv], dkv[:, hkv:], r.scale, True, ws, r.cu_dev)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(dq), ref[0])
+        assert np.array_equal(host(dkv)[:, :hkv], ref[1]) and np.array_equal(host(dkv)[:, hkv:], ref[2])
