@@ -78,7 +78,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="64k", choices=["tiny", "8k", "64k", "varlen", "256k"])
-    ap.add_argument("--cpu-tokens", type=int, default=3072,
+    ap.add_argument("--cpu-tokens", type=int, default=9216,
                     help="tokens of the oracle's CPU-baseline sample (0 = skip)")
     args = ap.parse_args()
 
