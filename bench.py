@@ -121,6 +121,7 @@ def main():
     dqkv_seq = torch.empty((n, w.Ht, d), dtype=torch.int16, device="cuda")
     ws = torch.empty(uly.attn_bwd_workspace_bytes(w.N, hq, hkv, d, 1 if cu is None else len(cu) - 1),
                      dtype=torch.uint8, device="cuda")
+    ws_fwd = torch.empty(uly.attn_fwd_workspace_bytes(w.N, hq, hkv, d), dtype=torch.uint8, device="cuda")
     o_chunks = o.view(P, n, hq, d)          # O's P destination chunks (token blocks)
     g_chunks = dqkv.view(P, n, ht, d)
 
@@ -128,7 +129,7 @@ def main():
              "a8_attn_bwd_dkdv", "a10_unpack_dqkv"]
     launches = [
         lambda: uly.ulysses_seq_to_head(x_seq, send, P, w.segments),
-        lambda: uly.attn_fwd(q, k, v, o, lse, w.scale, True, cu_dev, None),
+        lambda: uly.attn_fwd(q, k, v, o, lse, w.scale, True, cu_dev, None, ws_fwd),
         lambda: uly.ulysses_head_to_seq(o_chunks, o_seq, P, [w.Hq]),
         lambda: uly.ulysses_seq_to_head(dy_seq, dsend, P, [w.Hq]),
         lambda: uly.attn_bwd_dq(q, k, v, o, lse, dy_head, dq, w.scale, True, ws, cu_dev),

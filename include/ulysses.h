@@ -130,13 +130,21 @@ int ulysses_head_to_seq(const uint16_t *x_recv, uint16_t *x_seq, int64_t n_local
  * Query head h uses KV head h / (hq / hkv) (contiguous GQA groups).
  * scale: score multiplier (1/sqrt(d) usually); must be finite and > 0.
  * causal != 0: key j is visible to query i iff j <= i.
+ * ws: device workspace of at least attn_fwd_workspace_bytes(N, hq, hkv, d)
+ *        bytes, 256-byte aligned, not overlapping any tensor argument; its
+ *        contents on entry do not matter (it receives a transposed copy of V).
  * Errors: ULY_E_NULL, ULY_E_SHAPE, ULY_E_GQA, ULY_E_HEADDIM (d not 64/128),
- * ULY_E_STRIDE (a stride < heads*d), ULY_E_ALIGN, ULY_E_ALIAS (o overlaps q,
- * k or v), ULY_E_HIP.
+ * ULY_E_STRIDE (a stride < heads*d), ULY_E_ALIGN, ULY_E_WORKSPACE,
+ * ULY_E_ALIAS (o overlaps q, k or v, or ws overlaps a tensor), ULY_E_HIP.
  */
 int attn_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *o, float *lse,
              int64_t N, int32_t hq, int32_t hkv, int32_t d, int64_t q_stride, int64_t k_stride,
-             int64_t v_stride, int64_t o_stride, float scale, int32_t causal, hipStream_t stream);
+             int64_t v_stride, int64_t o_stride, float scale, int32_t causal, void *ws,
+             size_t ws_bytes, hipStream_t stream);
+
+/* Workspace attn_fwd and attn_fwd_varlen need: hkv * d * roundup(N, 64) * 2
+ * bytes, rounded up to 256. */
+size_t attn_fwd_workspace_bytes(int64_t N, int32_t hq, int32_t hkv, int32_t d);
 
 /*
  * attn_fwd over packed documents: key j is visible to query i iff both lie in
@@ -149,9 +157,12 @@ int attn_fwd_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v, uin
                     float *lse, int64_t N, int32_t hq, int32_t hkv, int32_t d, int64_t q_stride,
                     int64_t k_stride, int64_t v_stride, int64_t o_stride, float scale,
                     int32_t causal, const int32_t *cu_seqlens, int32_t n_seqs,
-                    int32_t max_seqlen, hipStream_t stream);
+                    int32_t max_seqlen, void *ws, size_t ws_bytes, hipStream_t stream);
 
-/* Workspace the backward pass needs (float32 D = rowsum(dO * O), [hq][N]). */
+/* Workspace the backward pass needs: float32 D = rowsum(dO * O) and
+ * LSE*log2(e), [hq][roundup(N, 64)] each, then transposed copies of K, Q and
+ * dO (hkv, hq and hq heads of d * roundup(N, 64) bf16), each region rounded
+ * up to 256 bytes. */
 size_t attn_bwd_workspace_bytes(int64_t N, int32_t hq, int32_t hkv, int32_t d, int32_t n_seqs);
 
 /*
@@ -187,9 +198,10 @@ int attn_bwd_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
  * on their own (e.g. to overlap the second with other work). attn_bwd is
  * exactly attn_bwd_dq followed by attn_bwd_dkdv on the same stream.
  *
- * attn_bwd_dq: D = rowsum(dout * o) into ws (float32 [hq][N]) and dq.
- * attn_bwd_dkdv: dk and dv, reading D from ws as left by attn_bwd_dq with the
- *   same arguments (ws must not be modified in between).
+ * attn_bwd_dq: fills ws (D, LSE*log2(e), the transposed copies of K, Q and
+ *   dO) and writes dq.
+ * attn_bwd_dkdv: dk and dv, reading ws as left by attn_bwd_dq with the same
+ *   arguments (ws must not be modified in between).
  * cu_seqlens: device table as in attn_fwd_varlen, or NULL for one document
  * (n_seqs is then ignored). Errors as attn_bwd.
  */

@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     attn_bwd_dq,
     attn_bwd_workspace_bytes,
     attn_fwd,
+    attn_fwd_workspace_bytes,
     raw,
     status_string,
     ulysses_check_cu_seqlens,

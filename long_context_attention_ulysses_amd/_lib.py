@@ -46,10 +46,11 @@ _SIGS = {
     "ulysses_check_cu_seqlens": ([ctypes.POINTER(_i32), _i32, _i64], ctypes.c_int),
     "ulysses_seq_to_head": ([_p, _p, _i64, _i32, _i32, ctypes.POINTER(_i32), _i32, _p], ctypes.c_int),
     "ulysses_head_to_seq": ([_p, _p, _i64, _i32, _i32, ctypes.POINTER(_i32), _i32, _p], ctypes.c_int),
-    "attn_fwd": ([_p, _p, _p, _p, _p, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _i64, _f32, _i32, _p],
-                 ctypes.c_int),
+    "attn_fwd": ([_p, _p, _p, _p, _p, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _i64, _f32, _i32, _p, _sz,
+                  _p], ctypes.c_int),
     "attn_fwd_varlen": ([_p, _p, _p, _p, _p, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _i64, _f32, _i32,
-                         _p, _i32, _i32, _p], ctypes.c_int),
+                         _p, _i32, _i32, _p, _sz, _p], ctypes.c_int),
+    "attn_fwd_workspace_bytes": ([_i64, _i32, _i32, _i32], _sz),
     "attn_bwd_workspace_bytes": ([_i64, _i32, _i32, _i32, _i32], _sz),
     "attn_bwd": ([_p] * 9 + [_i64, _i32, _i32, _i32] + [_i64] * 8 + [_f32, _i32, _p, _sz, _p], ctypes.c_int),
     "attn_bwd_varlen": ([_p] * 9 + [_i64, _i32, _i32, _i32] + [_i64] * 8 + [_f32, _i32, _p, _i32, _i32, _p, _sz,
@@ -136,20 +137,34 @@ def _tok_stride(t, heads, d):
     return t.stride(0)
 
 
+def attn_fwd_workspace_bytes(N: int, hq: int, hkv: int, d: int) -> int:
+    return int(_L.attn_fwd_workspace_bytes(N, hq, hkv, d))
+
+
+def _workspace(nbytes: int, like):
+    """Device memory for a workspace (torch's allocator; 256-byte aligned)."""
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=like.device)
+
+
 def attn_fwd(q, k, v, o, lse, scale: float, causal: bool = True, cu_seqlens=None,
-             max_seqlen: Optional[int] = None, stream=None) -> None:
+             max_seqlen: Optional[int] = None, ws=None, stream=None) -> None:
     """q [N, hq, d], k/v [N, hkv, d], o [N, hq, d] (views with any token stride);
-    lse [hq, N] float32. cu_seqlens: int32 device tensor [n_seqs + 1] or None."""
+    lse [hq, N] float32. cu_seqlens: int32 device tensor [n_seqs + 1] or None.
+    ws: device buffer of at least attn_fwd_workspace_bytes(...) bytes (one is
+    allocated when None)."""
     N, hq, d = q.shape
     hkv = k.shape[1]
+    if ws is None:
+        ws = _workspace(attn_fwd_workspace_bytes(N, hq, hkv, d), q)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), N, hq, hkv, d, _tok_stride(q, hq, d),
             _tok_stride(k, hkv, d), _tok_stride(v, hkv, d), _tok_stride(o, hq, d), float(scale), int(bool(causal)))
+    wsb = ws.numel() * ws.element_size()
     if cu_seqlens is None:
-        _check(_L.attn_fwd(*args, _stream(stream)), "attn_fwd")
+        _check(_L.attn_fwd(*args, _ptr(ws), wsb, _stream(stream)), "attn_fwd")
     else:
         n_seqs = cu_seqlens.numel() - 1
-        _check(_L.attn_fwd_varlen(*args, _ptr(cu_seqlens), n_seqs, int(max_seqlen or N), _stream(stream)),
-               "attn_fwd_varlen")
+        _check(_L.attn_fwd_varlen(*args, _ptr(cu_seqlens), n_seqs, int(max_seqlen or N), _ptr(ws), wsb,
+                                  _stream(stream)), "attn_fwd_varlen")
 
 
 def attn_bwd_workspace_bytes(N: int, hq: int, hkv: int, d: int, n_seqs: int = 1) -> int:
@@ -164,7 +179,7 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, scale: float, causal: bool = Tru
     hkv = k.shape[1]
     n_seqs = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
     if ws is None:
-        raise ValueError("attn_bwd needs a workspace tensor")
+        ws = _workspace(attn_bwd_workspace_bytes(N, hq, hkv, d, n_seqs), q)
     ws_bytes = ws.numel() * ws.element_size()
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
             N, hq, hkv, d, _tok_stride(q, hq, d), _tok_stride(k, hkv, d), _tok_stride(v, hkv, d),

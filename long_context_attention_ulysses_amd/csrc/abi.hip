@@ -85,7 +85,8 @@ int check_varlen_args(const int32_t *cu, int32_t n_seqs, int32_t max_seqlen, int
 int attn_fwd_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *o,
                   float *lse, int64_t N, int32_t hq, int32_t hkv, int32_t d, int64_t qs,
                   int64_t ks, int64_t vs, int64_t os, float scale, int32_t causal,
-                  const int32_t *cu, int32_t n_seqs, hipStream_t stream) {
+                  const int32_t *cu, int32_t n_seqs, void *ws, size_t ws_bytes,
+                  hipStream_t stream) {
   int rc = check_attn_common(q, k, v, N, hq, hkv, d, qs, ks, vs, scale);
   if (rc) return rc;
   if ((rc = check_out(o, N, os, (int64_t)hq * d))) return rc;
@@ -95,6 +96,14 @@ int attn_fwd_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint1
       overlaps(o, ob, k, span_bytes(N, ks, (int64_t)hkv * d)) ||
       overlaps(o, ob, v, span_bytes(N, vs, (int64_t)hkv * d)) ||
       overlaps(lse, (size_t)N * hq * 4, o, ob))
+    return ULY_E_ALIAS;
+  if (!ws || ws_bytes < fwd_ws_bytes(N, hkv, d) || (reinterpret_cast<uintptr_t>(ws) & 255u))
+    return ULY_E_WORKSPACE;
+  const size_t wb = fwd_ws_bytes(N, hkv, d);
+  if (overlaps(ws, wb, o, ob) || overlaps(ws, wb, lse, (size_t)N * hq * 4) ||
+      overlaps(ws, wb, q, span_bytes(N, qs, (int64_t)hq * d)) ||
+      overlaps(ws, wb, k, span_bytes(N, ks, (int64_t)hkv * d)) ||
+      overlaps(ws, wb, v, span_bytes(N, vs, (int64_t)hkv * d)))
     return ULY_E_ALIAS;
   AttnShape s;
   s.N = N;
@@ -109,7 +118,7 @@ int attn_fwd_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint1
   s.causal = causal ? 1 : 0;
   s.cu = cu;
   s.n_seqs = n_seqs;
-  return launch_attn_fwd(s, q, k, v, o, lse, stream);
+  return launch_attn_fwd(s, q, k, v, o, lse, ws, stream);
 }
 
 int attn_bwd_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *o,
@@ -130,7 +139,8 @@ int attn_bwd_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
   if (want_dkv && (rc = check_out(dk, N, dks, wk))) return rc;
   if (want_dkv && (rc = check_out(dv, N, dvs, wk))) return rc;
   if (!ws) return ULY_E_WORKSPACE;
-  if (ws_bytes < attn_bwd_workspace_bytes(N, hq, hkv, d, n_seqs)) return ULY_E_WORKSPACE;
+  const size_t wb = bwd_ws_layout(N, hq, hkv, d).total;
+  if (ws_bytes < wb) return ULY_E_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return ULY_E_WORKSPACE;
   // outputs must not overlap any input or the workspace (they may interleave
   // with each other, as views into one fused buffer)
@@ -144,7 +154,7 @@ int attn_bwd_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
                    {o, want_dq ? span_bytes(N, os, wq) : 0},
                    {dout, span_bytes(N, dos, wq)},
                    {lse, (size_t)N * hq * 4},
-                   {ws, (size_t)N * hq * 4}};
+                   {ws, wb}};
   const R outs[] = {{dq, want_dq ? span_bytes(N, dqs, wq) : 0},
                     {dk, want_dkv ? span_bytes(N, dks, wk) : 0},
                     {dv, want_dkv ? span_bytes(N, dvs, wk) : 0}};
@@ -178,7 +188,7 @@ int attn_bwd_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
   p.dq_stride = dqs;
   p.dk_stride = dks;
   p.dv_stride = dvs;
-  p.delta = static_cast<float *>(const_cast<void *>(ws));
+  p.ws = static_cast<char *>(const_cast<void *>(ws));
   return launch_attn_bwd(s, p, parts, stream);
 }
 
@@ -240,31 +250,35 @@ int ulysses_head_to_seq(const uint16_t *x_recv, uint16_t *x_seq, int64_t n_local
   return launch_swap(false, x_recv, x_seq, n_local, P, n_seg, seg_heads, d, stream);
 }
 
+size_t attn_fwd_workspace_bytes(int64_t N, int32_t hq, int32_t hkv, int32_t d) {
+  (void)hq;
+  if (N <= 0 || hkv <= 0 || d <= 0) return 0;
+  return fwd_ws_bytes(N, hkv, d);
+}
+
 int attn_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *o, float *lse,
              int64_t N, int32_t hq, int32_t hkv, int32_t d, int64_t q_stride, int64_t k_stride,
-             int64_t v_stride, int64_t o_stride, float scale, int32_t causal, hipStream_t stream) {
+             int64_t v_stride, int64_t o_stride, float scale, int32_t causal, void *ws,
+             size_t ws_bytes, hipStream_t stream) {
   return attn_fwd_impl(q, k, v, o, lse, N, hq, hkv, d, q_stride, k_stride, v_stride, o_stride,
-                       scale, causal, nullptr, 0, stream);
+                       scale, causal, nullptr, 0, ws, ws_bytes, stream);
 }
 
 int attn_fwd_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *o,
                     float *lse, int64_t N, int32_t hq, int32_t hkv, int32_t d, int64_t q_stride,
                     int64_t k_stride, int64_t v_stride, int64_t o_stride, float scale,
                     int32_t causal, const int32_t *cu_seqlens, int32_t n_seqs,
-                    int32_t max_seqlen, hipStream_t stream) {
+                    int32_t max_seqlen, void *ws, size_t ws_bytes, hipStream_t stream) {
   int rc = check_varlen_args(cu_seqlens, n_seqs, max_seqlen, N);
   if (rc) return rc;
   return attn_fwd_impl(q, k, v, o, lse, N, hq, hkv, d, q_stride, k_stride, v_stride, o_stride,
-                       scale, causal, cu_seqlens, n_seqs, stream);
+                       scale, causal, cu_seqlens, n_seqs, ws, ws_bytes, stream);
 }
 
 size_t attn_bwd_workspace_bytes(int64_t N, int32_t hq, int32_t hkv, int32_t d, int32_t n_seqs) {
-  (void)hkv;
-  (void)d;
   (void)n_seqs;
-  if (N <= 0 || hq <= 0) return 0;
-  const size_t bytes = (size_t)N * (size_t)hq * sizeof(float);
-  return (bytes + 255) & ~(size_t)255;
+  if (N <= 0 || hq <= 0 || hkv <= 0 || d <= 0) return 0;
+  return bwd_ws_layout(N, hq, hkv, d).total;
 }
 
 int attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *o,

@@ -10,20 +10,19 @@
 //   dK_j  = scale * sum_{heads of the group} sum_i ds_ij q_i
 //   dV_j  = sum_{heads of the group} sum_i p_ij dO_i
 //
-// Two kernels, no atomics (the result is deterministic):
-//   1. dq kernel, parallel over (query block, head): computes D for its rows
-//      (written to the workspace), then loops over key tiles:
-//      S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T.
-//      K and V tiles are staged in LDS row-major, plus K^T in contraction
-//      order; Q and dO stay in registers as MFMA B operands.
+// Two kernels, no atomics (the result is deterministic). Operands whose
+// contraction index is the token come from contraction-ordered transposed
+// copies (K^T, Q^T, dO^T, written once per call into the workspace); all
+// tiles stream into LDS with direct-to-LDS copies and are read with 16-byte
+// loads only.
+//   1. dq kernel, parallel over (query block, head): D and LSE*log2(e) for
+//      its rows (to the workspace), then per 64-key tile (3-stage ring):
+//      S^T = K Q^T, dP^T = V dO^T, P^T, dS^T, dQ^T += K^T dS^T
+//      (Q and dO stay in registers as B operands; a lane owns one query).
 //   2. dkdv kernel, parallel over (key block, KV head): loops over the query
-//      heads of the group and their query tiles:
-//      S = Q K^T, dP = dO V^T (K, V in registers), P, dS,
-//      dV^T += dO^T P, dK^T += Q^T dS. Q, dO tiles are staged in LDS both
-//      row-major and transposed, with the rows' LSE and D.
-// Orientation: in kernel 1 a lane owns one query (scores transposed), in
-// kernel 2 a lane owns one key, so the per-row quantities (LSE, D, mask
-// bounds) are always a lane scalar or a short LDS read.
+//      heads of the group and their 64-query tiles (2-stage ring):
+//      S = Q K^T, dP = dO V^T (K, V in registers; a lane owns one key),
+//      P, dS, dV^T += dO^T P, dK^T += Q^T dS.
 #include "attn_common.h"
 #include "uly_internal.h"
 
@@ -35,8 +34,9 @@ struct BwdArgs {
   const bf16_t *q, *k, *v, *o, *dout;
   const float *lse;
   bf16_t *dq, *dk, *dv;
-  float *delta;
-  int64_t N;
+  float *delta, *lse2;             // workspace [hq][Np]
+  const bf16_t *kt, *qt, *dot;     // workspace: contraction-ordered transposes
+  int64_t N, Np;
   int64_t q_stride, k_stride, v_stride, o_stride, do_stride, dq_stride, dk_stride, dv_stride;
   int hq, hkv, G;
   int nblk, nhg;  // blocks along the sequence, head groups
@@ -58,22 +58,18 @@ struct DqCfg {
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int JS = BN / 16;
-  static constexpr int KROW = D + 8;
-  static constexpr int K_ELEMS = BN * KROW;
-  static constexpr int V_ELEMS = BN * KROW;
-  static constexpr int KT_ELEMS = D * BN;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS + KT_ELEMS;
-  static constexpr int K_UNITS = (BN / 2) * (D / 8);  // (key pair, d chunk)
-  static constexpr int K_PER_T = (K_UNITS + NT - 1) / NT;
-  static constexpr int V_VECS = BN * D / 8;
-  static constexpr int V_PER_T = (V_VECS + NT - 1) / NT;
-  static constexpr size_t LDS_BYTES = 2 * STAGE * sizeof(bf16_t);
+  static constexpr int TILE = BN * D;
+  static constexpr int NI = TILE / 512;    // 1 KiB copies per tile and tensor
+  static_assert(NI % NW == 0, "copies must split evenly over the waves");
+  static constexpr int NLW = 3 * NI / NW;  // copies per wave per tile (K, V, K^T)
 };
 
 template <int D, int HPW, int RB>
 __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_bwd_dq_kernel(BwdArgs a) {
   using C = DqCfg<D, HPW, RB>;
-  extern __shared__ __align__(16) bf16_t smem[];
+  __shared__ __align__(16) bf16_t k0[C::TILE], k1[C::TILE], k2[C::TILE];
+  __shared__ __align__(16) bf16_t v0[C::TILE], v1[C::TILE], v2[C::TILE];
+  __shared__ __align__(16) bf16_t t0_[C::TILE], t1_[C::TILE], t2_[C::TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -130,7 +126,10 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_bwd_dq_kernel(BwdArgs a
   }
   const float delta = dpart + xor32(dpart);
   const float lse2 = row_ok ? a.lse[(int64_t)h * a.N + row] * kLog2e : 0.f;
-  if (row_ok && hi32 == 0) a.delta[(int64_t)h * a.N + row] = delta;
+  if (row_ok && hi32 == 0) {
+    a.delta[(int64_t)h * a.Np + row] = delta;
+    a.lse2[(int64_t)h * a.Np + row] = lse2;
+  }
 
   f32x16 acc[C::DB];
 #pragma unroll
@@ -142,140 +141,98 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_bwd_dq_kernel(BwdArgs a
   const int kt1 = (int)((kv_hi + C::BN - 1) / C::BN);
   const bf16_t *kbase = a.k + (int64_t)g * D;
   const bf16_t *vbase = a.v + (int64_t)g * D;
+  const bf16_t *ktbase = a.kt + (int64_t)g * D * a.Np;
 
-  u32x4 kreg[C::K_PER_T][2];
-  u32x4 vreg[C::V_PER_T];
-
-  auto load_tile = [&](int kt) {
+  auto issue = [&](int kt, bf16_t *ks_, bf16_t *vs_, bf16_t *ts_) {
     const int64_t t0 = (int64_t)kt * C::BN;
 #pragma unroll
-    for (int u = 0; u < C::K_PER_T; ++u) {
-      const int idx = tid + u * C::NT;
-      const int kp = idx / (D / 8);
-      const int dc = idx % (D / 8);
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        u32x4 v = {0, 0, 0, 0};
-        const int64_t key = t0 + 2 * kp + r;
-        if (idx < C::K_UNITS && key < a.N)
-          v = *reinterpret_cast<const u32x4 *>(kbase + key * a.k_stride + dc * 8);
-        kreg[u][r] = v;
-      }
+    for (int i = 0; i < C::NI / C::NW; ++i) {
+      const int u = w + i * C::NW;
+      const int s = u * 64 + lane;
+      const int r = s / (D / 8);
+      const int c = (s % (D / 8)) ^ row_swz<D>(r);
+      const int64_t key = (t0 + r < a.N) ? t0 + r : a.N - 1;  // rows past N are masked
+      dma16(kbase + key * a.k_stride + c * 8, lds_ptr(ks_ + u * 512));
+      dma16(vbase + key * a.v_stride + c * 8, lds_ptr(vs_ + u * 512));
     }
 #pragma unroll
-    for (int u = 0; u < C::V_PER_T; ++u) {
-      const int idx = tid + u * C::NT;
-      const int key = idx / (D / 8);
-      const int dc = idx % (D / 8);
-      u32x4 v = {0, 0, 0, 0};
-      if (idx < C::V_VECS && t0 + key < a.N)
-        v = *reinterpret_cast<const u32x4 *>(vbase + (t0 + key) * a.v_stride + dc * 8);
-      vreg[u] = v;
+    for (int i = 0; i < C::NI / C::NW; ++i) {
+      const int u = w + i * C::NW;
+      const int s = u * 64 + lane;
+      const int d = s >> 3;
+      const int c = (s & 7) ^ ((d >> 1) & 7);
+      dma16(ktbase + (int64_t)d * a.Np + t0 + c * 8, lds_ptr(ts_ + u * 512));
     }
   };
 
-  auto store_tile = [&](int stage) {
-    bf16_t *ks_ = smem + stage * C::STAGE;
-    bf16_t *vs_ = ks_ + C::K_ELEMS;
-    bf16_t *kt_ = vs_ + C::V_ELEMS;
-#pragma unroll
-    for (int u = 0; u < C::K_PER_T; ++u) {
-      const int idx = tid + u * C::NT;
-      if (idx < C::K_UNITS) {
-        const int kp = idx / (D / 8);
-        const int dc = idx % (D / 8);
-        *reinterpret_cast<u32x4 *>(ks_ + (2 * kp) * C::KROW + dc * 8) = kreg[u][0];
-        *reinterpret_cast<u32x4 *>(ks_ + (2 * kp + 1) * C::KROW + dc * 8) = kreg[u][1];
-        const int p = key_pos(2 * kp);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t lo = (kreg[u][0][e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-          const uint32_t hi = (kreg[u][1][e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-          *reinterpret_cast<uint32_t *>(kt_ + tr_off(dc * 8 + e, p)) = lo | (hi << 16);
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < C::V_PER_T; ++u) {
-      const int idx = tid + u * C::NT;
-      if (idx < C::V_VECS) {
-        const int key = idx / (D / 8);
-        const int dc = idx % (D / 8);
-        *reinterpret_cast<u32x4 *>(vs_ + key * C::KROW + dc * 8) = vreg[u];
-      }
-    }
-  };
-
-  if (kt0 < kt1) {
-    load_tile(kt0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const int stage = (kt - kt0) & 1;
-    if (kt + 1 < kt1) load_tile(kt + 1);
+  auto compute = [&](int kt, const bf16_t *ks_, const bf16_t *vs_, const bf16_t *ts_) {
     const int64_t t0 = (int64_t)kt * C::BN;
-    if (wave_valid && t0 < w_hi && t0 + C::BN > w_lo) {
-      const bf16_t *ks_ = smem + stage * C::STAGE;
-      const bf16_t *vs_ = ks_ + C::K_ELEMS;
-      const bf16_t *kt_ = vs_ + C::V_ELEMS;
-      f32x16 s[2], dp[2];
+    if (!(wave_valid && t0 < w_hi && t0 + C::BN > w_lo)) return;
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[kb][i] = 0.f;
+        dp[kb][i] = 0.f;
+      }
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int off = rt_off<D>(kb * 32 + l32, ks * 2 + hi32);
+        const bf16x8 ak = as_bf16x8(*reinterpret_cast<const u32x4 *>(ks_ + off));
+        const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4 *>(vs_ + off));
+        s[kb] = mfma32(ak, qf[ks], s[kb]);
+        dp[kb] = mfma32(av, dof[ks], dp[kb]);
+      }
+    }
+    if ((t0 < w_lo_max) || (t0 + C::BN > w_hi_min)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          s[kb][i] = 0.f;
-          dp[kb][i] = 0.f;
+          const int64_t key = t0 + kb * 32 + (i >> 2) * 8 + hi32 * 4 + (i & 3);
+          if (key < rlo || key >= rhi) s[kb][i] = -INFINITY;
         }
+    }
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int off = (kb * 32 + l32) * C::KROW + ks * 16 + hi32 * 8;
-          const bf16x8 ak = as_bf16x8(*reinterpret_cast<const u32x4 *>(ks_ + off));
-          const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4 *>(vs_ + off));
-          s[kb] = mfma32(ak, qf[ks], s[kb]);
-          dp[kb] = mfma32(av, dof[ks], dp[kb]);
-        }
-      }
-      const bool need_mask = (t0 < w_lo_max) || (t0 + C::BN > w_hi_min);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int64_t key = t0 + kb * 32 + (i >> 2) * 8 + hi32 * 4 + (i & 3);
-            if (key < rlo || key >= rhi) s[kb][i] = -INFINITY;
-          }
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.c, -lse2));
+        s[kb][i] = p * (dp[kb][i] - delta);  // dS^T
       }
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int j = 0; j < C::JS; ++j) {
+      const f32x16 &sv = s[j >> 1];
+      const int b = (j & 1) * 8;
+      const bf16x8 dsf =
+          cvt8(sv[b + 0], sv[b + 1], sv[b + 2], sv[b + 3], sv[b + 4], sv[b + 5], sv[b + 6], sv[b + 7]);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.c, -lse2));
-          s[kb][i] = p * (dp[kb][i] - delta);  // dS^T
-        }
-      bf16x8 dsf[C::JS];
-#pragma unroll
-      for (int j = 0; j < C::JS; ++j) {
-        const f32x16 &sv = s[j >> 1];
-        const int b = (j & 1) * 8;
-        dsf[j] = cvt8(sv[b + 0], sv[b + 1], sv[b + 2], sv[b + 3], sv[b + 4], sv[b + 5], sv[b + 6],
-                      sv[b + 7]);
-      }
-#pragma unroll
-      for (int j = 0; j < C::JS; ++j) {
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const bf16x8 ak = as_bf16x8(
-              *reinterpret_cast<const u32x4 *>(kt_ + tr_off(db * 32 + l32, j * 16 + hi32 * 8)));
-          acc[db] = mfma32(ak, dsf[j], acc[db]);
-        }
+      for (int db = 0; db < C::DB; ++db) {
+        const bf16x8 ak =
+            as_bf16x8(*reinterpret_cast<const u32x4 *>(ts_ + tr_off(db * 32 + l32, 2 * j + hi32)));
+        acc[db] = mfma32(ak, dsf, acc[db]);
       }
     }
-    if (kt + 1 < kt1) store_tile(stage ^ 1);
-    __syncthreads();
+  };
+
+  auto step = [&](int t, const bf16_t *ks_, const bf16_t *vs_, const bf16_t *ts_, bf16_t *kn,
+                  bf16_t *vn, bf16_t *tn) {
+    if (t + 1 < kt1) wait_vmcnt<C::NLW>();
+    else wait_vmcnt<0>();
+    barrier();
+    if (t + 2 < kt1) issue(t + 2, kn, vn, tn);
+    compute(t, ks_, vs_, ts_);
+  };
+
+  if (kt0 < kt1) issue(kt0, k0, v0, t0_);
+  if (kt0 + 1 < kt1) issue(kt0 + 1, k1, v1, t1_);
+  for (int kt = kt0; kt < kt1; kt += 3) {
+    step(kt, k0, v0, t0_, k2, v2, t2_);
+    if (kt + 1 < kt1) step(kt + 1, k1, v1, t1_, k0, v0, t0_);
+    if (kt + 2 < kt1) step(kt + 2, k2, v2, t2_, k1, v1, t1_);
   }
 
   if (row_ok) {
@@ -302,20 +259,19 @@ struct DkvCfg {
   static constexpr int BQ = 64;         // queries per tile
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int KROW = D + 8;
-  static constexpr int Q_ELEMS = BQ * KROW;
-  static constexpr int QT_ELEMS = D * BQ;
-  // stage: Q, dO (row-major), Q^T, dO^T (transposed), then lse2[BQ], delta[BQ] floats
-  static constexpr int STAGE = 2 * Q_ELEMS + 2 * QT_ELEMS + 2 * BQ * 2;
-  static constexpr int UNITS = (BQ / 2) * (D / 8);  // (query pair, d chunk)
-  static constexpr int U_PER_T = (UNITS + NT - 1) / NT;
-  static constexpr size_t LDS_BYTES = 2 * STAGE * sizeof(bf16_t);
+  static constexpr int TILE = BQ * D;
+  static constexpr int NI = TILE / 512;  // 1 KiB copies per tile and tensor
+  static_assert(NI % NWK == 0, "copies must split evenly over the waves");
 };
 
 template <int D, int NWK>
 __global__ void __launch_bounds__(NWK * 64, 1) attn_bwd_dkdv_kernel(BwdArgs a) {
   using C = DkvCfg<D, NWK>;
-  extern __shared__ __align__(16) bf16_t smem[];
+  __shared__ __align__(16) bf16_t q0s[C::TILE], q1s[C::TILE];    // Q row tiles
+  __shared__ __align__(16) bf16_t d0s[C::TILE], d1s[C::TILE];    // dO row tiles
+  __shared__ __align__(16) bf16_t qt0[C::TILE], qt1[C::TILE];    // Q^T trans tiles
+  __shared__ __align__(16) bf16_t dt0[C::TILE], dt1[C::TILE];    // dO^T trans tiles
+  __shared__ __align__(16) float ls0[2 * C::BQ], ls1[2 * C::BQ];  // LSE*log2e, D
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -373,150 +329,128 @@ __global__ void __launch_bounds__(NWK * 64, 1) attn_bwd_dkdv_kernel(BwdArgs a) {
       acc_dv[db][i] = 0.f;
     }
 
-  const int qt0 = (int)(qr_lo / C::BQ);
-  const int qt1 = (int)((qr_hi + C::BQ - 1) / C::BQ);
-  const int ntq = qt1 - qt0;
+  const int qt0_ = (int)(qr_lo / C::BQ);
+  const int qt1_ = (int)((qr_hi + C::BQ - 1) / C::BQ);
+  const int ntq = qt1_ - qt0_;
   const int ntiles = ntq * a.G;  // (head of the group, query tile) pairs
 
-  u32x4 qreg[C::U_PER_T][2], dreg[C::U_PER_T][2];
-  float lreg = 0.f;
-
-  auto load_tile = [&](int t) {
-    const int hh = t / ntq;
-    const int h = g * a.G + hh;
-    const int64_t u0 = (int64_t)(qt0 + t % ntq) * C::BQ;
+  auto issue = [&](int t, bf16_t *qs, bf16_t *ds, bf16_t *qts, bf16_t *dts, float *ls) {
+    const int h = g * a.G + t / ntq;
+    const int64_t u0 = (int64_t)(qt0_ + t % ntq) * C::BQ;
+    const bf16_t *qb_ = a.q + (int64_t)h * D;
+    const bf16_t *db_ = a.dout + (int64_t)h * D;
 #pragma unroll
-    for (int u = 0; u < C::U_PER_T; ++u) {
-      const int idx = tid + u * C::NT;
-      const int qp = idx / (D / 8);
-      const int dc = idx % (D / 8);
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        u32x4 vq = {0, 0, 0, 0}, vd = {0, 0, 0, 0};
-        const int64_t qi = u0 + 2 * qp + r;
-        if (idx < C::UNITS && qi < a.N) {
-          const int64_t col = (int64_t)h * D + dc * 8;
-          vq = *reinterpret_cast<const u32x4 *>(a.q + qi * a.q_stride + col);
-          vd = *reinterpret_cast<const u32x4 *>(a.dout + qi * a.do_stride + col);
-        }
-        qreg[u][r] = vq;
-        dreg[u][r] = vd;
-      }
+    for (int i = 0; i < C::NI / NWK; ++i) {
+      const int u = w + i * NWK;
+      const int s = u * 64 + lane;
+      const int r = s / (D / 8);
+      const int c = (s % (D / 8)) ^ row_swz<D>(r);
+      const int64_t qi = (u0 + r < a.N) ? u0 + r : a.N - 1;  // rows past N are masked
+      dma16(qb_ + qi * a.q_stride + c * 8, lds_ptr(qs + u * 512));
+      dma16(db_ + qi * a.do_stride + c * 8, lds_ptr(ds + u * 512));
     }
-    lreg = 0.f;
-    if (tid < 2 * C::BQ) {
-      const int64_t qi = u0 + (tid % C::BQ);
-      if (qi < a.N)
-        lreg = (tid < C::BQ) ? a.lse[(int64_t)h * a.N + qi] * kLog2e : a.delta[(int64_t)h * a.N + qi];
+    const bf16_t *qtb = a.qt + (int64_t)h * D * a.Np + u0;
+    const bf16_t *dtb = a.dot + (int64_t)h * D * a.Np + u0;
+#pragma unroll
+    for (int i = 0; i < C::NI / NWK; ++i) {
+      const int u = w + i * NWK;
+      const int s = u * 64 + lane;
+      const int d = s >> 3;
+      const int c = (s & 7) ^ ((d >> 1) & 7);
+      dma16(qtb + (int64_t)d * a.Np + c * 8, lds_ptr(qts + u * 512));
+      dma16(dtb + (int64_t)d * a.Np + c * 8, lds_ptr(dts + u * 512));
+    }
+    if (w < 2) {  // wave 0: LSE*log2e of the 64 rows, wave 1: D
+      const float *src = (w == 0 ? a.lse2 : a.delta) + (int64_t)h * a.Np;
+      const int64_t qi = (u0 + lane < a.N) ? u0 + lane : a.N - 1;
+      dma4(src + qi, lds_ptr(ls + w * C::BQ));
     }
   };
 
-  auto store_tile = [&](int stage) {
-    bf16_t *qs = smem + stage * C::STAGE;
-    bf16_t *ds = qs + C::Q_ELEMS;
-    bf16_t *qts = ds + C::Q_ELEMS;
-    bf16_t *dts = qts + C::QT_ELEMS;
-    float *ls = reinterpret_cast<float *>(dts + C::QT_ELEMS);
+  auto compute = [&](int t, const bf16_t *qs, const bf16_t *ds, const bf16_t *qts, const bf16_t *dts,
+                     const float *ls) {
+    const int64_t u0 = (int64_t)(qt0_ + t % ntq) * C::BQ;
+    if (!(wave_valid && u0 < w_hi && u0 + C::BQ > w_lo)) return;
+    const bool need_mask = (u0 < w_lo_max) || (u0 + C::BQ > w_hi_min);
+    f32x16 s[2], dp[2];
 #pragma unroll
-    for (int u = 0; u < C::U_PER_T; ++u) {
-      const int idx = tid + u * C::NT;
-      if (idx < C::UNITS) {
-        const int qp = idx / (D / 8);
-        const int dc = idx % (D / 8);
-        *reinterpret_cast<u32x4 *>(qs + (2 * qp) * C::KROW + dc * 8) = qreg[u][0];
-        *reinterpret_cast<u32x4 *>(qs + (2 * qp + 1) * C::KROW + dc * 8) = qreg[u][1];
-        *reinterpret_cast<u32x4 *>(ds + (2 * qp) * C::KROW + dc * 8) = dreg[u][0];
-        *reinterpret_cast<u32x4 *>(ds + (2 * qp + 1) * C::KROW + dc * 8) = dreg[u][1];
-        const int p = key_pos(2 * qp);
+    for (int qb2 = 0; qb2 < 2; ++qb2)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int sh = (e & 1) * 16;
-          const uint32_t q0v = (qreg[u][0][e >> 1] >> sh) & 0xFFFFu;
-          const uint32_t q1v = (qreg[u][1][e >> 1] >> sh) & 0xFFFFu;
-          const uint32_t d0v = (dreg[u][0][e >> 1] >> sh) & 0xFFFFu;
-          const uint32_t d1v = (dreg[u][1][e >> 1] >> sh) & 0xFFFFu;
-          *reinterpret_cast<uint32_t *>(qts + tr_off(dc * 8 + e, p)) = q0v | (q1v << 16);
-          *reinterpret_cast<uint32_t *>(dts + tr_off(dc * 8 + e, p)) = d0v | (d1v << 16);
-        }
+      for (int i = 0; i < 16; ++i) {
+        s[qb2][i] = 0.f;
+        dp[qb2][i] = 0.f;
       }
-    }
-    if (tid < 2 * C::BQ) ls[tid] = lreg;
-  };
-
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int stage = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
-    const int64_t u0 = (int64_t)(qt0 + t % ntq) * C::BQ;
-    if (wave_valid && u0 < w_hi && u0 + C::BQ > w_lo) {
-      const bf16_t *qs = smem + stage * C::STAGE;
-      const bf16_t *ds = qs + C::Q_ELEMS;
-      const bf16_t *qts = ds + C::Q_ELEMS;
-      const bf16_t *dts = qts + C::QT_ELEMS;
-      const float *ls = reinterpret_cast<const float *>(dts + C::QT_ELEMS);
-      const bool need_mask = (u0 < w_lo_max) || (u0 + C::BQ > w_hi_min);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
 #pragma unroll
       for (int qb2 = 0; qb2 < 2; ++qb2) {
-        f32x16 s, dp;
+        const int off = rt_off<D>(qb2 * 32 + l32, ks * 2 + hi32);
+        const bf16x8 aq = as_bf16x8(*reinterpret_cast<const u32x4 *>(qs + off));
+        const bf16x8 ad = as_bf16x8(*reinterpret_cast<const u32x4 *>(ds + off));
+        s[qb2] = mfma32(aq, kf[ks], s[qb2]);
+        dp[qb2] = mfma32(ad, vf[ks], dp[qb2]);
+      }
+    }
+#pragma unroll
+    for (int qb2 = 0; qb2 < 2; ++qb2) {
+      if (need_mask) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          s[i] = 0.f;
-          dp[i] = 0.f;
+          const int64_t qi = u0 + qb2 * 32 + (i >> 2) * 8 + hi32 * 4 + (i & 3);
+          if (qi < qlo || qi >= qhi) s[qb2][i] = -INFINITY;
         }
+      }
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-          const int off = (qb2 * 32 + l32) * C::KROW + ks * 16 + hi32 * 8;
-          const bf16x8 aq = as_bf16x8(*reinterpret_cast<const u32x4 *>(qs + off));
-          const bf16x8 ad = as_bf16x8(*reinterpret_cast<const u32x4 *>(ds + off));
-          s = mfma32(aq, kf[ks], s);
-          dp = mfma32(ad, vf[ks], dp);
-        }
-        if (need_mask) {
+      for (int gq = 0; gq < 4; ++gq) {
+        const int qo = qb2 * 32 + gq * 8 + hi32 * 4;
+        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(ls + qo);
+        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(ls + C::BQ + qo);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int64_t qi = u0 + qb2 * 32 + (i >> 2) * 8 + hi32 * 4 + (i & 3);
-            if (qi < qlo || qi >= qhi) s[i] = -INFINITY;
-          }
-        }
-        float pv[16], dsv[16];
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int qo = qb2 * 32 + gq * 8 + hi32 * 4;
-          const f32x4 l4 = *reinterpret_cast<const f32x4 *>(ls + qo);
-          const f32x4 d4 = *reinterpret_cast<const f32x4 *>(ls + C::BQ + qo);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = gq * 4 + e;
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[i], a.c, -l4[e]));
-            pv[i] = p;
-            dsv[i] = p * (dp[i] - d4[e]);
-          }
-        }
-#pragma unroll
-        for (int jq = 0; jq < 2; ++jq) {
-          const int b = jq * 8;
-          const bf16x8 pf = cvt8(pv[b + 0], pv[b + 1], pv[b + 2], pv[b + 3], pv[b + 4], pv[b + 5],
-                                 pv[b + 6], pv[b + 7]);
-          const bf16x8 sf = cvt8(dsv[b + 0], dsv[b + 1], dsv[b + 2], dsv[b + 3], dsv[b + 4],
-                                 dsv[b + 5], dsv[b + 6], dsv[b + 7]);
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db) {
-            const int off = tr_off(db * 32 + l32, qb2 * 32 + jq * 16 + hi32 * 8);
-            const bf16x8 adt = as_bf16x8(*reinterpret_cast<const u32x4 *>(dts + off));
-            const bf16x8 aqt = as_bf16x8(*reinterpret_cast<const u32x4 *>(qts + off));
-            acc_dv[db] = mfma32(adt, pf, acc_dv[db]);
-            acc_dk[db] = mfma32(aqt, sf, acc_dk[db]);
-          }
+        for (int e = 0; e < 4; ++e) {
+          const int i = gq * 4 + e;
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[qb2][i], a.c, -l4[e]));
+          s[qb2][i] = p;
+          dp[qb2][i] = p * (dp[qb2][i] - d4[e]);  // dS
         }
       }
     }
-    if (t + 1 < ntiles) store_tile(stage ^ 1);
-    __syncthreads();
+#pragma unroll
+    for (int qb2 = 0; qb2 < 2; ++qb2) {
+#pragma unroll
+      for (int jq = 0; jq < 2; ++jq) {
+        const int b = jq * 8;
+        const f32x16 &pv = s[qb2];
+        const f32x16 &sv = dp[qb2];
+        const bf16x8 pf = cvt8(pv[b + 0], pv[b + 1], pv[b + 2], pv[b + 3], pv[b + 4], pv[b + 5], pv[b + 6],
+                               pv[b + 7]);
+        const bf16x8 sf = cvt8(sv[b + 0], sv[b + 1], sv[b + 2], sv[b + 3], sv[b + 4], sv[b + 5], sv[b + 6],
+                               sv[b + 7]);
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const int off = tr_off(db * 32 + l32, qb2 * 4 + jq * 2 + hi32);
+          const bf16x8 adt = as_bf16x8(*reinterpret_cast<const u32x4 *>(dts + off));
+          const bf16x8 aqt = as_bf16x8(*reinterpret_cast<const u32x4 *>(qts + off));
+          acc_dv[db] = mfma32(adt, pf, acc_dv[db]);
+          acc_dk[db] = mfma32(aqt, sf, acc_dk[db]);
+        }
+      }
+    }
+  };
+
+  // Two stages: wait for tile t, barrier (tile t complete, the other stage
+  // free), prefetch t+1 into the other stage, compute t.
+  if (ntiles > 0) issue(0, q0s, d0s, qt0, dt0, ls0);
+  for (int t = 0; t < ntiles; t += 2) {
+    wait_vmcnt<0>();
+    barrier();
+    if (t + 1 < ntiles) issue(t + 1, q1s, d1s, qt1, dt1, ls1);
+    compute(t, q0s, d0s, qt0, dt0, ls0);
+    if (t + 1 < ntiles) {
+      wait_vmcnt<0>();
+      barrier();
+      if (t + 2 < ntiles) issue(t + 2, q0s, d0s, qt0, dt0, ls0);
+      compute(t + 1, q1s, d1s, qt1, dt1, ls1);
+    }
   }
 
   if (key_ok) {
@@ -543,12 +477,9 @@ int launch_dq_cfg(BwdArgs a, hipStream_t stream) {
   using C = DqCfg<D, HPW, RB>;
   a.nblk = (int)((a.N + C::BM - 1) / C::BM);
   a.nhg = a.hq / HPW;
-  hipError_t e = hipFuncSetAttribute((const void *)attn_bwd_dq_kernel<D, HPW, RB>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
-  if (e != hipSuccess) return set_hip_error(e, "attn_bwd dq: hipFuncSetAttribute");
   hipLaunchKernelGGL((attn_bwd_dq_kernel<D, HPW, RB>), dim3((unsigned)((int64_t)a.nblk * a.nhg)),
-                     dim3(C::NT), C::LDS_BYTES, stream, a);
-  e = hipGetLastError();
+                     dim3(C::NT), 0, stream, a);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_hip_error(e, "attn_bwd_dq_kernel");
   return 0;
 }
@@ -557,12 +488,9 @@ template <int D, int NWK>
 int launch_dkdv_cfg(BwdArgs a, hipStream_t stream) {
   using C = DkvCfg<D, NWK>;
   a.nblk = (int)((a.N + C::BNK - 1) / C::BNK);
-  hipError_t e = hipFuncSetAttribute((const void *)attn_bwd_dkdv_kernel<D, NWK>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
-  if (e != hipSuccess) return set_hip_error(e, "attn_bwd dkdv: hipFuncSetAttribute");
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, NWK>), dim3((unsigned)((int64_t)a.nblk * a.hkv)),
-                     dim3(C::NT), C::LDS_BYTES, stream, a);
-  e = hipGetLastError();
+                     dim3(C::NT), 0, stream, a);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_hip_error(e, "attn_bwd_dkdv_kernel");
   return 0;
 }
@@ -570,6 +498,7 @@ int launch_dkdv_cfg(BwdArgs a, hipStream_t stream) {
 }  // namespace
 
 int launch_attn_bwd(const AttnShape &s, const AttnBwdPtrs &p, int parts, hipStream_t stream) {
+  const BwdWs L = bwd_ws_layout(s.N, s.hq, s.hkv, s.d);
   BwdArgs a;
   a.q = p.q;
   a.k = p.k;
@@ -580,8 +509,13 @@ int launch_attn_bwd(const AttnShape &s, const AttnBwdPtrs &p, int parts, hipStre
   a.dq = p.dq;
   a.dk = p.dk;
   a.dv = p.dv;
-  a.delta = p.delta;
+  a.delta = reinterpret_cast<float *>(p.ws + L.delta);
+  a.lse2 = reinterpret_cast<float *>(p.ws + L.lse2);
+  a.kt = reinterpret_cast<const bf16_t *>(p.ws + L.kt);
+  a.qt = reinterpret_cast<const bf16_t *>(p.ws + L.qt);
+  a.dot = reinterpret_cast<const bf16_t *>(p.ws + L.dot);
   a.N = s.N;
+  a.Np = pad64(s.N);
   a.q_stride = s.q_stride;
   a.k_stride = s.k_stride;
   a.v_stride = s.v_stride;
@@ -601,20 +535,27 @@ int launch_attn_bwd(const AttnShape &s, const AttnBwdPtrs &p, int parts, hipStre
   a.n_seqs = s.n_seqs;
   const int hpw = (a.G % 4 == 0) ? 4 : (a.G % 2 == 0) ? 2 : 1;
   int rc = 0;
-  if (s.d == 128) {
-    if (parts & 1)
-      rc = hpw == 4 ? launch_dq_cfg<128, 4, 1>(a, stream)
-           : hpw == 2 ? launch_dq_cfg<128, 2, 2>(a, stream)
-                      : launch_dq_cfg<128, 1, 4>(a, stream);
+  if (parts & 1) {
+    // Transposed copies for both kernels: K^T for this one, Q^T and dO^T for
+    // the dK/dV kernel (made here so that kernel runs alone).
+    bf16_t *ws_kt = reinterpret_cast<bf16_t *>(p.ws + L.kt);
+    bf16_t *ws_qt = reinterpret_cast<bf16_t *>(p.ws + L.qt);
+    bf16_t *ws_dot = reinterpret_cast<bf16_t *>(p.ws + L.dot);
+    if ((rc = launch_to_trans(p.k, s.k_stride, s.hkv, s.d, s.N, ws_kt, stream))) return rc;
+    if ((rc = launch_to_trans(p.q, s.q_stride, s.hq, s.d, s.N, ws_qt, stream))) return rc;
+    if ((rc = launch_to_trans(p.dout, p.do_stride, s.hq, s.d, s.N, ws_dot, stream))) return rc;
+    if (s.d == 128)
+      rc = hpw == 4 ? launch_dq_cfg<128, 4, 2>(a, stream)
+           : hpw == 2 ? launch_dq_cfg<128, 2, 4>(a, stream)
+                      : launch_dq_cfg<128, 1, 8>(a, stream);
+    else
+      rc = hpw == 4 ? launch_dq_cfg<64, 4, 2>(a, stream)
+           : hpw == 2 ? launch_dq_cfg<64, 2, 4>(a, stream)
+                      : launch_dq_cfg<64, 1, 8>(a, stream);
     if (rc) return rc;
-    return (parts & 2) ? launch_dkdv_cfg<128, 4>(a, stream) : 0;
   }
-  if (parts & 1)
-    rc = hpw == 4 ? launch_dq_cfg<64, 4, 2>(a, stream)
-         : hpw == 2 ? launch_dq_cfg<64, 2, 4>(a, stream)
-                    : launch_dq_cfg<64, 1, 8>(a, stream);
-  if (rc) return rc;
-  return (parts & 2) ? launch_dkdv_cfg<64, 4>(a, stream) : 0;
+  if (parts & 2) rc = s.d == 128 ? launch_dkdv_cfg<128, 4>(a, stream) : launch_dkdv_cfg<64, 4>(a, stream);
+  return rc;
 }
 
 }  // namespace uly

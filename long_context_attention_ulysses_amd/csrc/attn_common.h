@@ -44,14 +44,65 @@ __device__ __forceinline__ bf16x8 cvt8(float a0, float a1, float a2, float a3, f
   return as_bf16x8(r);
 }
 
-// Element offset of (row r, position p) in a transposed LDS tile whose rows
-// hold 64 positions (keys or queries, in MFMA-contraction order). The eight
-// 16-byte chunks of a row are XOR-swizzled with bits 1..3 of the row so that
-// sixteen consecutive rows read at one chunk position hit distinct banks.
-__device__ __forceinline__ int tr_off(int r, int p) {
-  const int chunk = (p >> 3) ^ ((r >> 1) & 7);
-  return r * 64 + (chunk << 3) + (p & 7);
+#define ULY_LDS __attribute__((address_space(3)))
+
+// ---- LDS tiles -------------------------------------------------------------
+// Two tile shapes, both 64 rows/positions deep and filled by direct-to-LDS
+// copies (global_load_lds_dwordx4: lane i's 16 bytes land at base + 16 i, so
+// any permutation of 16-byte chunks inside a 1 KiB block is free to build):
+//
+//   row tile   [64 rows][D]: a token's d values in one row; the 16-byte
+//              chunks of row r are XOR-swizzled so that 16 consecutive rows
+//              read at one chunk position hit 16 distinct bank groups.
+//   trans tile [D rows][64 positions]: one row per d, positions in MFMA
+//              contraction order; chunks XOR-swizzled with bits 1..3 of the
+//              row for the same reason (a row is half the 256-byte bank width).
+// Both are read with ds_read_b128 only (a row tile as the [row][k] operand,
+// a trans tile as the [d][position] operand).
+
+// Swizzle of row tile row r (chunk index space of D/8 chunks).
+template <int D>
+__device__ __forceinline__ int row_swz(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
 }
+
+// Element offset of logical 16-byte chunk c of row r in a row tile.
+template <int D>
+__device__ __forceinline__ int rt_off(int r, int c) {
+  return r * D + ((c ^ row_swz<D>(r)) << 3);
+}
+
+// Element offset of logical 16-byte chunk c (positions 8c..8c+7) of row r in
+// a trans tile.
+__device__ __forceinline__ int tr_off(int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 7)) << 3); }
+
+// Wave-wide direct-to-LDS copy of 16 bytes per lane: lane i's bytes from
+// `src` land at lds + 16 i. `lds` must be wave-uniform.
+__device__ __forceinline__ void dma16(const void *src, ULY_LDS void *lds) {
+  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
+
+// Same with 4 bytes per lane (lane i -> lds + 4 i).
+__device__ __forceinline__ void dma4(const void *src, ULY_LDS void *lds) {
+  __builtin_amdgcn_global_load_lds(src, lds, 4, 0, 0);
+}
+
+template <typename T>
+__device__ __forceinline__ ULY_LDS void *lds_ptr(T *p) {
+  return (ULY_LDS void *)p;
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (s_waitcnt vmcnt(N); the other counters are left unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without a memory fence: LDS tiles written by
+// direct-to-LDS copies are covered by the explicit vmcnt waits before it.
+__device__ __forceinline__ void barrier() { __builtin_amdgcn_s_barrier(); }
 
 // Value of lane l ^ 32.
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }

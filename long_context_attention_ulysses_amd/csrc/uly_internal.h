@@ -18,6 +18,38 @@ int set_hip_error(hipError_t e, const char *where);
 int launch_swap(bool to_head, const bf16_t *src, bf16_t *dst, int64_t n, int P, int nseg,
                 const int32_t *seg_heads, int d, hipStream_t stream);
 
+__host__ __device__ inline int64_t pad64(int64_t n) { return (n + 63) / 64 * 64; }
+
+inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Writes xt[h][d][pad64(N)]: the contraction-ordered, transposed copy of the
+// `heads` heads of x (token stride xs), zero beyond N.
+int launch_to_trans(const bf16_t *x, int64_t xs, int heads, int d, int64_t N, bf16_t *xt,
+                    hipStream_t stream);
+
+// Forward workspace: V^T [hkv][d][pad64(N)].
+inline size_t fwd_ws_bytes(int64_t N, int hkv, int d) {
+  return align256((size_t)hkv * d * pad64(N) * sizeof(bf16_t));
+}
+
+// Backward workspace regions (byte offsets): D and LSE*log2(e) as float
+// [hq][pad64(N)], then K^T, Q^T, dO^T as contraction-ordered bf16 copies.
+struct BwdWs {
+  size_t delta, lse2, kt, qt, dot, total;
+};
+
+inline BwdWs bwd_ws_layout(int64_t N, int hq, int hkv, int d) {
+  const size_t np = (size_t)pad64(N);
+  BwdWs w;
+  w.delta = 0;
+  w.lse2 = w.delta + align256((size_t)hq * np * 4);
+  w.kt = w.lse2 + align256((size_t)hq * np * 4);
+  w.qt = w.kt + align256((size_t)hkv * d * np * 2);
+  w.dot = w.qt + align256((size_t)hq * d * np * 2);
+  w.total = w.dot + align256((size_t)hq * d * np * 2);
+  return w;
+}
+
 // Attention problem description shared by the forward and backward launches.
 struct AttnShape {
   int64_t N;
@@ -29,15 +61,16 @@ struct AttnShape {
   int n_seqs;
 };
 
+// ws: fwd_ws_bytes(N, hkv, d) bytes, 256-byte aligned.
 int launch_attn_fwd(const AttnShape &s, const bf16_t *q, const bf16_t *k, const bf16_t *v,
-                    bf16_t *o, float *lse, hipStream_t stream);
+                    bf16_t *o, float *lse, void *ws, hipStream_t stream);
 
 struct AttnBwdPtrs {
   const bf16_t *q, *k, *v, *o, *dout;
   const float *lse;
   bf16_t *dq, *dk, *dv;
   int64_t do_stride, dq_stride, dk_stride, dv_stride;
-  float *delta;  // workspace: D = rowsum(dO * O), [hq][N] float32
+  char *ws;  // workspace laid out by bwd_ws_layout
 };
 
 // parts: 1 = D and dQ, 2 = dK and dV (reads D), 3 = both in that order.

@@ -13,10 +13,14 @@ HEADER = os.path.join(ROOT, "include", "ulysses.h")
 uly = pytest.importorskip("long_context_attention_ulysses_amd")
 L = uly.raw()
 
-A = 1 << 20           # a fake, 16-byte aligned "device" address (never dereferenced)
-B = 2 << 20
-C = 3 << 20
-D_ = 4 << 20
+# fake, 256-byte aligned "device" addresses 32 MiB apart (never dereferenced)
+A = 1 << 25
+B = 2 << 25
+C = 3 << 25
+D_ = 4 << 25
+E = 5 << 25       # lse
+F = 6 << 25       # dout / cu
+W = 8 << 25       # workspace
 
 
 def declared_functions():
@@ -72,11 +76,11 @@ def test_swap_validation(args, code):
 
 
 def _fwd(**kw):
-    a = dict(q=A, k=B, v=C, o=D_, lse=5 << 20, N=1024, hq=8, hkv=2, d=128, qs=1536, ks=1536, vs=1536,
-             os=1024, scale=0.088, causal=1)
+    a = dict(q=A, k=B, v=C, o=D_, lse=E, N=1024, hq=8, hkv=2, d=128, qs=1536, ks=1536, vs=1536,
+             os=1024, scale=0.088, causal=1, ws=W, wsb=1 << 24)
     a.update(kw)
     return L.attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["N"], a["hq"], a["hkv"], a["d"], a["qs"],
-                      a["ks"], a["vs"], a["os"], a["scale"], a["causal"], None)
+                      a["ks"], a["vs"], a["os"], a["scale"], a["causal"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -92,29 +96,34 @@ def _fwd(**kw):
     (dict(scale=0.0), "ULY_E_SHAPE"),
     (dict(scale=float("nan")), "ULY_E_SHAPE"),
     (dict(o=A), "ULY_E_ALIAS"),
+    (dict(ws=0), "ULY_E_WORKSPACE"),
+    (dict(wsb=100), "ULY_E_WORKSPACE"),
+    (dict(ws=W + 64), "ULY_E_WORKSPACE"),
+    (dict(ws=D_), "ULY_E_ALIAS"),
 ])
 def test_attn_fwd_validation(kw, code):
     assert _fwd(**kw) == uly.CODE[code]
 
 
 def test_attn_varlen_and_bwd_validation():
-    r = L.attn_fwd_varlen(A, B, C, D_, 5 << 20, 1024, 8, 2, 128, 1536, 1536, 1536, 1024, 0.1, 1, None, 3, 512,
-                          None)
+    r = L.attn_fwd_varlen(A, B, C, D_, E, 1024, 8, 2, 128, 1536, 1536, 1536, 1024, 0.1, 1, None, 3, 512,
+                          W, 1 << 24, None)
     assert r == uly.CODE["ULY_E_NULL"]
-    r = L.attn_fwd_varlen(A, B, C, D_, 5 << 20, 1024, 8, 2, 128, 1536, 1536, 1536, 1024, 0.1, 1, 6 << 20, 0, 512,
-                          None)
+    r = L.attn_fwd_varlen(A, B, C, D_, E, 1024, 8, 2, 128, 1536, 1536, 1536, 1024, 0.1, 1, F, 0, 512,
+                          W, 1 << 24, None)
     assert r == uly.CODE["ULY_E_SHAPE"]
     N, hq, hkv, d = 1024, 8, 2, 128
     need = L.attn_bwd_workspace_bytes(N, hq, hkv, d, 1)
-    assert need >= N * hq * 4 and need % 256 == 0
+    assert need >= N * hq * 4 * 2 + N * d * (hkv + 2 * hq) * 2 and need % 256 == 0
+    assert L.attn_fwd_workspace_bytes(N, hq, hkv, d) == hkv * d * N * 2
 
-    def bwd(ws=7 << 20, ws_bytes=need, dq=8 << 20, dk=9 << 20, dv=10 << 20):
-        return L.attn_bwd(A, B, C, D_, 5 << 20, 6 << 20, dq, dk, dv, N, hq, hkv, d, 1536, 1536, 1536, 1024, 1024,
+    def bwd(ws=W, ws_bytes=need, dq=9 << 25, dk=10 << 25, dv=11 << 25):
+        return L.attn_bwd(A, B, C, D_, E, F, dq, dk, dv, N, hq, hkv, d, 1536, 1536, 1536, 1024, 1024,
                           1536, 1536, 1536, 0.1, 1, ws, ws_bytes, None)
 
     assert bwd(ws=0) == uly.CODE["ULY_E_WORKSPACE"]
     assert bwd(ws_bytes=need - 1) == uly.CODE["ULY_E_WORKSPACE"]
-    assert bwd(ws=(7 << 20) + 16) == uly.CODE["ULY_E_WORKSPACE"]
+    assert bwd(ws=W + 16) == uly.CODE["ULY_E_WORKSPACE"]
     assert bwd(dq=A) == uly.CODE["ULY_E_ALIAS"]
-    assert bwd(dk=7 << 20) == uly.CODE["ULY_E_ALIAS"]
+    assert bwd(dk=W + (1 << 20)) == uly.CODE["ULY_E_ALIAS"]
     assert bwd(dv=0) == uly.CODE["ULY_E_NULL"]
