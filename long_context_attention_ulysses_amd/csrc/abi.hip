@@ -20,6 +20,9 @@ namespace {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// N rows of `stride` elements stay below 2 GiB of bf16 (byte offsets fit 31 bits).
+bool fits_rows(int64_t N, int64_t stride) { return N * stride < ((int64_t)1 << 30); }
+
 // [a, a + na) and [b, b + nb) overlap (byte ranges).
 bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
@@ -62,6 +65,9 @@ int check_attn_common(const void *q, const void *k, const void *v, int64_t N, in
   if (d != 64 && d != 128) return ULY_E_HEADDIM;
   if (qs < (int64_t)hq * d || ks < (int64_t)hkv * d || vs < (int64_t)hkv * d) return ULY_E_STRIDE;
   if (qs % 8 || ks % 8 || vs % 8) return ULY_E_ALIGN;
+  // the kernels address one head's rows with 32-bit byte offsets
+  if (!fits_rows(N, qs) || !fits_rows(N, ks) || !fits_rows(N, vs) || !fits_rows(pad64(N), d))
+    return ULY_E_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return ULY_E_ALIGN;
   return ULY_OK;
 }
@@ -133,6 +139,7 @@ int attn_bwd_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
   if (!lse || !dout || (want_dq && !o)) return ULY_E_NULL;
   const int64_t wq = (int64_t)hq * d, wk = (int64_t)hkv * d;
   if (dos < wq || (want_dq && os < wq)) return ULY_E_STRIDE;
+  if (!fits_rows(N, dos)) return ULY_E_SHAPE;
   if (dos % 8 || (want_dq && os % 8)) return ULY_E_ALIGN;
   if (!aligned16(dout) || (want_dq && !aligned16(o))) return ULY_E_ALIGN;
   if (want_dq && (rc = check_out(dq, N, dqs, wq))) return rc;

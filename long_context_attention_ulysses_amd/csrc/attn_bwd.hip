@@ -139,29 +139,32 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_bwd_dq_kernel(BwdArgs a
 
   const int kt0 = (int)(kv_lo / C::BN);
   const int kt1 = (int)((kv_hi + C::BN - 1) / C::BN);
-  const bf16_t *kbase = a.k + (int64_t)g * D;
-  const bf16_t *vbase = a.v + (int64_t)g * D;
-  const bf16_t *ktbase = a.kt + (int64_t)g * D * a.Np;
+  // Buffer views: K and V rows of KV head g (rows >= N read as zeros; their
+  // scores are masked) and K^T of head g.
+  const uint32_t ksb = (uint32_t)(a.k_stride * 2), vsb = (uint32_t)(a.v_stride * 2);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + (int64_t)g * D, head_rows_bytes(a.N, a.k_stride, D));
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v + (int64_t)g * D, head_rows_bytes(a.N, a.v_stride, D));
+  const __amdgpu_buffer_rsrc_t trs = make_rsrc(a.kt + (int64_t)g * D * a.Np, (uint32_t)(D * a.Np * 2));
+  uint32_t koff[C::NI / C::NW], voff[C::NI / C::NW], toff[C::NI / C::NW];
+#pragma unroll
+  for (int i = 0; i < C::NI / C::NW; ++i) {
+    const int s = (w + i * C::NW) * 64 + lane;
+    const int r = s / (D / 8);
+    const uint32_t cb = ((s % (D / 8)) ^ row_swz<D>(r)) << 4;
+    koff[i] = r * ksb + cb;
+    voff[i] = r * vsb + cb;
+    const int d = s >> 3;
+    toff[i] = (uint32_t)(d * a.Np * 2) + (((s & 7) ^ ((d >> 1) & 7)) << 4);
+  }
 
   auto issue = [&](int kt, bf16_t *ks_, bf16_t *vs_, bf16_t *ts_) {
-    const int64_t t0 = (int64_t)kt * C::BN;
+    const uint32_t t0 = (uint32_t)kt * C::BN;
 #pragma unroll
     for (int i = 0; i < C::NI / C::NW; ++i) {
       const int u = w + i * C::NW;
-      const int s = u * 64 + lane;
-      const int r = s / (D / 8);
-      const int c = (s % (D / 8)) ^ row_swz<D>(r);
-      const int64_t key = (t0 + r < a.N) ? t0 + r : a.N - 1;  // rows past N are masked
-      dma16(kbase + key * a.k_stride + c * 8, lds_ptr(ks_ + u * 512));
-      dma16(vbase + key * a.v_stride + c * 8, lds_ptr(vs_ + u * 512));
-    }
-#pragma unroll
-    for (int i = 0; i < C::NI / C::NW; ++i) {
-      const int u = w + i * C::NW;
-      const int s = u * 64 + lane;
-      const int d = s >> 3;
-      const int c = (s & 7) ^ ((d >> 1) & 7);
-      dma16(ktbase + (int64_t)d * a.Np + t0 + c * 8, lds_ptr(ts_ + u * 512));
+      dma16(krs, koff[i] + t0 * ksb, 0, lds_ptr(ks_ + u * 512));
+      dma16(vrs, voff[i] + t0 * vsb, 0, lds_ptr(vs_ + u * 512));
+      dma16(trs, toff[i], t0 * 2, lds_ptr(ts_ + u * 512));
     }
   };
 
@@ -334,36 +337,41 @@ __global__ void __launch_bounds__(NWK * 64, 1) attn_bwd_dkdv_kernel(BwdArgs a) {
   const int ntq = qt1_ - qt0_;
   const int ntiles = ntq * a.G;  // (head of the group, query tile) pairs
 
+  // Per-lane byte offsets of this wave's 16-byte slots inside a tile: row
+  // tiles of Q and dO (token stride), trans tiles of Q^T and dO^T.
+  const uint32_t qsb = (uint32_t)(a.q_stride * 2), dsb = (uint32_t)(a.do_stride * 2);
+  uint32_t qoff[C::NI / NWK], doff[C::NI / NWK], toff[C::NI / NWK];
+#pragma unroll
+  for (int i = 0; i < C::NI / NWK; ++i) {
+    const int s = (w + i * NWK) * 64 + lane;
+    const int r = s / (D / 8);
+    const uint32_t cb = ((s % (D / 8)) ^ row_swz<D>(r)) << 4;
+    qoff[i] = r * qsb + cb;
+    doff[i] = r * dsb + cb;
+    const int d = s >> 3;
+    toff[i] = (uint32_t)(d * a.Np * 2) + (((s & 7) ^ ((d >> 1) & 7)) << 4);
+  }
+
   auto issue = [&](int t, bf16_t *qs, bf16_t *ds, bf16_t *qts, bf16_t *dts, float *ls) {
     const int h = g * a.G + t / ntq;
-    const int64_t u0 = (int64_t)(qt0_ + t % ntq) * C::BQ;
-    const bf16_t *qb_ = a.q + (int64_t)h * D;
-    const bf16_t *db_ = a.dout + (int64_t)h * D;
+    const uint32_t u0 = (uint32_t)(qt0_ + t % ntq) * C::BQ;
+    // Q and dO rows of head h (rows >= N read as zeros; they are masked).
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.q + (int64_t)h * D, head_rows_bytes(a.N, a.q_stride, D));
+    const __amdgpu_buffer_rsrc_t drs =
+        make_rsrc(a.dout + (int64_t)h * D, head_rows_bytes(a.N, a.do_stride, D));
+    const __amdgpu_buffer_rsrc_t qtr = make_rsrc(a.qt + (int64_t)h * D * a.Np, (uint32_t)(D * a.Np * 2));
+    const __amdgpu_buffer_rsrc_t dtr = make_rsrc(a.dot + (int64_t)h * D * a.Np, (uint32_t)(D * a.Np * 2));
 #pragma unroll
     for (int i = 0; i < C::NI / NWK; ++i) {
       const int u = w + i * NWK;
-      const int s = u * 64 + lane;
-      const int r = s / (D / 8);
-      const int c = (s % (D / 8)) ^ row_swz<D>(r);
-      const int64_t qi = (u0 + r < a.N) ? u0 + r : a.N - 1;  // rows past N are masked
-      dma16(qb_ + qi * a.q_stride + c * 8, lds_ptr(qs + u * 512));
-      dma16(db_ + qi * a.do_stride + c * 8, lds_ptr(ds + u * 512));
+      dma16(qrs, qoff[i] + u0 * qsb, 0, lds_ptr(qs + u * 512));
+      dma16(drs, doff[i] + u0 * dsb, 0, lds_ptr(ds + u * 512));
+      dma16(qtr, toff[i], u0 * 2, lds_ptr(qts + u * 512));
+      dma16(dtr, toff[i], u0 * 2, lds_ptr(dts + u * 512));
     }
-    const bf16_t *qtb = a.qt + (int64_t)h * D * a.Np + u0;
-    const bf16_t *dtb = a.dot + (int64_t)h * D * a.Np + u0;
-#pragma unroll
-    for (int i = 0; i < C::NI / NWK; ++i) {
-      const int u = w + i * NWK;
-      const int s = u * 64 + lane;
-      const int d = s >> 3;
-      const int c = (s & 7) ^ ((d >> 1) & 7);
-      dma16(qtb + (int64_t)d * a.Np + c * 8, lds_ptr(qts + u * 512));
-      dma16(dtb + (int64_t)d * a.Np + c * 8, lds_ptr(dts + u * 512));
-    }
-    if (w < 2) {  // wave 0: LSE*log2e of the 64 rows, wave 1: D
+    if (w < 2) {  // wave 0: LSE*log2e of the 64 rows, wave 1: D (padded rows, masked)
       const float *src = (w == 0 ? a.lse2 : a.delta) + (int64_t)h * a.Np;
-      const int64_t qi = (u0 + lane < a.N) ? u0 + lane : a.N - 1;
-      dma4(src + qi, lds_ptr(ls + w * C::BQ));
+      dma4(make_rsrc(src, (uint32_t)(a.Np * 4)), lane * 4, u0 * 4, lds_ptr(ls + w * C::BQ));
     }
   };
 

@@ -76,15 +76,31 @@ __device__ __forceinline__ int rt_off(int r, int c) {
 // a trans tile.
 __device__ __forceinline__ int tr_off(int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 7)) << 3); }
 
-// Wave-wide direct-to-LDS copy of 16 bytes per lane: lane i's bytes from
-// `src` land at lds + 16 i. `lds` must be wave-uniform.
-__device__ __forceinline__ void dma16(const void *src, ULY_LDS void *lds) {
-  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+// Buffer resource over the `bytes` bytes at `base`: buffer loads at byte
+// offsets >= bytes return zeros (raw buffer, stride 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Wave-wide direct-to-LDS copy of 16 bytes per lane from buffer `r` at byte
+// offset voff + soff (voff per lane, soff wave-uniform): lane i's bytes land
+// at lds + 16 i. `lds` must be wave-uniform. Range checking uses voff only.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                      ULY_LDS void *lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, soff, 0, 0);
 }
 
 // Same with 4 bytes per lane (lane i -> lds + 4 i).
-__device__ __forceinline__ void dma4(const void *src, ULY_LDS void *lds) {
-  __builtin_amdgcn_global_load_lds(src, lds, 4, 0, 0);
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                     ULY_LDS void *lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 4, voff, soff, 0, 0);
+}
+
+// Bytes from the start of a head's first row to the end of its row N-1 in a
+// [N][heads][d] bf16 tensor with token stride `stride` (elements): the
+// buffer range of one head's rows, so rows >= N read as zeros.
+__host__ __device__ __forceinline__ uint32_t head_rows_bytes(int64_t N, int64_t stride, int d) {
+  return (uint32_t)(((N - 1) * stride + d) * 2);
 }
 
 template <typename T>

@@ -127,29 +127,31 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_fwd_kernel(FwdArgs a) {
 
   const int kt0 = (int)(kv_lo / C::BN);
   const int kt1 = (int)((kv_hi + C::BN - 1) / C::BN);
-  const bf16_t *kbase = a.k + (int64_t)g * D;
-  const bf16_t *vtbase = a.vt + (int64_t)g * D * a.Np;
+  // Buffer views: K rows of KV head g (rows >= N read as zeros, and their
+  // scores are masked) and V^T of head g.
+  const uint32_t kstride_b = (uint32_t)(a.k_stride * 2);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + (int64_t)g * D, head_rows_bytes(a.N, a.k_stride, D));
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.vt + (int64_t)g * D * a.Np, (uint32_t)(D * a.Np * 2));
+  // Per-lane byte offsets of this wave's 16-byte slots inside a tile.
+  uint32_t koff[C::NI / C::NW], voff[C::NI / C::NW];
+#pragma unroll
+  for (int i = 0; i < C::NI / C::NW; ++i) {
+    const int s = (w + i * C::NW) * 64 + lane;
+    const int r = s / (D / 8);
+    koff[i] = r * kstride_b + (((s % (D / 8)) ^ row_swz<D>(r)) << 4);
+    const int d = s >> 3;
+    voff[i] = (uint32_t)(d * a.Np * 2) + (((s & 7) ^ ((d >> 1) & 7)) << 4);
+  }
 
   // Direct-to-LDS copies of tile kt: this wave's share of the 1 KiB blocks.
   auto issue = [&](int kt, bf16_t *ks_, bf16_t *vs_) {
-    const int64_t t0 = (int64_t)kt * C::BN;
+    const uint32_t t0 = (uint32_t)kt * C::BN;
 #pragma unroll
-    for (int i = 0; i < C::NI / C::NW; ++i) {
-      const int u = w + i * C::NW;
-      const int s = u * 64 + lane;  // slot (16-byte chunk) of the row tile
-      const int r = s / (D / 8);
-      const int c = (s % (D / 8)) ^ row_swz<D>(r);
-      const int64_t key = (t0 + r < a.N) ? t0 + r : a.N - 1;  // rows past N are masked
-      dma16(kbase + key * a.k_stride + c * 8, lds_ptr(ks_ + u * 512));
-    }
+    for (int i = 0; i < C::NI / C::NW; ++i)
+      dma16(krs, koff[i] + t0 * kstride_b, 0, lds_ptr(ks_ + (w + i * C::NW) * 512));
 #pragma unroll
-    for (int i = 0; i < C::NI / C::NW; ++i) {
-      const int u = w + i * C::NW;
-      const int s = u * 64 + lane;  // slot of the trans tile
-      const int d = s >> 3;
-      const int c = (s & 7) ^ ((d >> 1) & 7);
-      dma16(vtbase + (int64_t)d * a.Np + t0 + c * 8, lds_ptr(vs_ + u * 512));
-    }
+    for (int i = 0; i < C::NI / C::NW; ++i)
+      dma16(vrs, voff[i], t0 * 2, lds_ptr(vs_ + (w + i * C::NW) * 512));
   };
 
   auto compute = [&](int kt, const bf16_t *ks_, const bf16_t *vs_) {
