@@ -72,6 +72,40 @@ def cpu_baseline(w, tokens: int):
     }
 
 
+KERNEL_OF = {"a3_attn_fwd": "attn_fwd_kernel", "a7a9_attn_bwd_dq": "attn_bwd_dq_kernel",
+             "a8_attn_bwd_dkdv": "attn_bwd_dkdv_kernel"}
+
+
+def csrc_digest():
+    """sha256 over the HIP sources (names and bytes), to tell whether stored
+    counter readings still describe the kernels being run."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "long_context_attention_ulysses_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, step_name: str):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary (profiles/traffic_<workload>.txt, counters scaled by the
+    readings of a copy of known size), or None when there is no summary for
+    this workload or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.txt" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        doc = json.load(fh)
+    if doc.get("source_sha256") != csrc_digest():
+        return None
+    prefix = KERNEL_OF[step_name]
+    hits = [d["hbm_bytes"] for d in doc["dispatches"] if d["kernel"].startswith(prefix)]
+    return hits[0] if len(hits) == 1 else None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -208,7 +242,7 @@ def main():
             "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(args.workload, dom),
         },
         "attn_tflops": round(total_flops / (attn_ms * 1e-3) / 1e12, 2),
         "attn_frac_peak": round(total_flops / (attn_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),

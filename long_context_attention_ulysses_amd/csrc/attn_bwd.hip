@@ -19,8 +19,9 @@
 //      its rows (to the workspace), then per 64-key tile (3-stage ring):
 //      S^T = K Q^T, dP^T = V dO^T, P^T, dS^T, dQ^T += K^T dS^T
 //      (Q and dO stay in registers as B operands; a lane owns one query).
-//   2. dkdv kernel, parallel over (key block, KV head): loops over the query
-//      heads of the group and their 64-query tiles (2-stage ring):
+//   2. dkdv kernel, parallel over (key block, KV head): loops over its
+//      64-query tiles from the last one down, the group's heads innermost
+//      (2-stage ring; concurrent workgroups walk the same tiles in step):
 //      S = Q K^T, dP = dO V^T (K, V in registers; a lane owns one key),
 //      P, dS, dV^T += dO^T P, dK^T += Q^T dS.
 #include "attn_common.h"
@@ -352,9 +353,15 @@ __global__ void __launch_bounds__(NWK * 64, 1) attn_bwd_dkdv_kernel(BwdArgs a) {
     toff[i] = (uint32_t)(d * a.Np * 2) + (((s & 7) ^ ((d >> 1) & 7)) << 4);
   }
 
+  // Tile t: query tiles from the last one down (every workgroup of a wave of
+  // launches starts on the same tiles and walks them in step, so they are
+  // shared through L2), the group's heads innermost.
+  auto tile_head = [&](int t) { return g * a.G + t % a.G; };
+  auto tile_u0 = [&](int t) { return (uint32_t)(qt1_ - 1 - t / a.G) * C::BQ; };
+
   auto issue = [&](int t, bf16_t *qs, bf16_t *ds, bf16_t *qts, bf16_t *dts, float *ls) {
-    const int h = g * a.G + t / ntq;
-    const uint32_t u0 = (uint32_t)(qt0_ + t % ntq) * C::BQ;
+    const int h = tile_head(t);
+    const uint32_t u0 = tile_u0(t);
     // Q and dO rows of head h (rows >= N read as zeros; they are masked).
     const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.q + (int64_t)h * D, head_rows_bytes(a.N, a.q_stride, D));
     const __amdgpu_buffer_rsrc_t drs =
@@ -377,35 +384,39 @@ __global__ void __launch_bounds__(NWK * 64, 1) attn_bwd_dkdv_kernel(BwdArgs a) {
 
   auto compute = [&](int t, const bf16_t *qs, const bf16_t *ds, const bf16_t *qts, const bf16_t *dts,
                      const float *ls) {
-    const int64_t u0 = (int64_t)(qt0_ + t % ntq) * C::BQ;
+    const int64_t u0 = tile_u0(t);
     if (!(wave_valid && u0 < w_hi && u0 + C::BQ > w_lo)) return;
     const bool need_mask = (u0 < w_lo_max) || (u0 + C::BQ > w_hi_min);
-    f32x16 s[2], dp[2];
+    {
+      constexpr int QB0 = 0, QBN = 2;  // both 32-query halves of the tile at once
+      f32x16 s[QBN], dp[QBN];
 #pragma unroll
-    for (int qb2 = 0; qb2 < 2; ++qb2)
+    for (int qi_ = 0; qi_ < QBN; ++qi_)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        s[qb2][i] = 0.f;
-        dp[qb2][i] = 0.f;
+        s[qi_][i] = 0.f;
+        dp[qi_][i] = 0.f;
       }
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
 #pragma unroll
-      for (int qb2 = 0; qb2 < 2; ++qb2) {
+      for (int qi_ = 0; qi_ < QBN; ++qi_) {
+        const int qb2 = QB0 + qi_;
         const int off = rt_off<D>(qb2 * 32 + l32, ks * 2 + hi32);
         const bf16x8 aq = as_bf16x8(*reinterpret_cast<const u32x4 *>(qs + off));
         const bf16x8 ad = as_bf16x8(*reinterpret_cast<const u32x4 *>(ds + off));
-        s[qb2] = mfma32(aq, kf[ks], s[qb2]);
-        dp[qb2] = mfma32(ad, vf[ks], dp[qb2]);
+        s[qi_] = mfma32(aq, kf[ks], s[qi_]);
+        dp[qi_] = mfma32(ad, vf[ks], dp[qi_]);
       }
     }
 #pragma unroll
-    for (int qb2 = 0; qb2 < 2; ++qb2) {
+    for (int qi_ = 0; qi_ < QBN; ++qi_) {
+      const int qb2 = QB0 + qi_;
       if (need_mask) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int64_t qi = u0 + qb2 * 32 + (i >> 2) * 8 + hi32 * 4 + (i & 3);
-          if (qi < qlo || qi >= qhi) s[qb2][i] = -INFINITY;
+          if (qi < qlo || qi >= qhi) s[qi_][i] = -INFINITY;
         }
       }
 #pragma unroll
@@ -416,19 +427,20 @@ __global__ void __launch_bounds__(NWK * 64, 1) attn_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = gq * 4 + e;
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[qb2][i], a.c, -l4[e]));
-          s[qb2][i] = p;
-          dp[qb2][i] = p * (dp[qb2][i] - d4[e]);  // dS
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[qi_][i], a.c, -l4[e]));
+          s[qi_][i] = p;
+          dp[qi_][i] = p * (dp[qi_][i] - d4[e]);  // dS
         }
       }
     }
 #pragma unroll
-    for (int qb2 = 0; qb2 < 2; ++qb2) {
+    for (int qi_ = 0; qi_ < QBN; ++qi_) {
+      const int qb2 = QB0 + qi_;
 #pragma unroll
       for (int jq = 0; jq < 2; ++jq) {
         const int b = jq * 8;
-        const f32x16 &pv = s[qb2];
-        const f32x16 &sv = dp[qb2];
+        const f32x16 &pv = s[qi_];
+        const f32x16 &sv = dp[qi_];
         const bf16x8 pf = cvt8(pv[b + 0], pv[b + 1], pv[b + 2], pv[b + 3], pv[b + 4], pv[b + 5], pv[b + 6],
                                pv[b + 7]);
         const bf16x8 sf = cvt8(sv[b + 0], sv[b + 1], sv[b + 2], sv[b + 3], sv[b + 4], sv[b + 5], sv[b + 6],
@@ -442,6 +454,7 @@ __global__ void __launch_bounds__(NWK * 64, 1) attn_bwd_dkdv_kernel(BwdArgs a) {
           acc_dk[db] = mfma32(aqt, sf, acc_dk[db]);
         }
       }
+    }
     }
   };
 
