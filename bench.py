@@ -106,6 +106,69 @@ def measured_traffic(workload: str, step_name: str):
     return hits[0] if len(hits) == 1 else None
 
 
+def short_kernel_name(full: str) -> str:
+    """'void uly::(anonymous namespace)::f<128, 4>(args)' -> 'f<128, 4>'."""
+    name = full.replace("(anonymous namespace)::", "")
+    name = name.split("(")[0].replace("void ", "", 1)
+    return name.split("::")[-1].strip()
+
+
+def write_traffic_summary(workload: str, pmc_dir: str):
+    """Turn two rocprofv3 counter runs of `bench.py --steps 1 --warmup 0`
+    (FETCH_SIZE in <pmc_dir>/fetch_counter_collection.csv, WRITE_SIZE in
+    <pmc_dir>/write_counter_collection.csv) into profiles/traffic_<workload>.txt.
+    Both counters are scaled by what they read for the step's first launch,
+    the seq->head pack, which reads and writes exactly the sequence shard's
+    bytes once."""
+    import csv
+
+    import workloads
+    w = workloads.WORKLOADS[workload]
+
+    def read(name, counter):
+        rows = []
+        with open(os.path.join(pmc_dir, "%s_counter_collection.csv" % name)) as fh:
+            for r in csv.DictReader(fh):
+                assert r["Counter_Name"] == counter, r["Counter_Name"]
+                rows.append((int(r["Dispatch_Id"]), short_kernel_name(r["Kernel_Name"]),
+                             float(r["Counter_Value"])))
+        return sorted(rows)
+
+    fetch, write = read("fetch", "FETCH_SIZE"), read("write", "WRITE_SIZE")
+    assert [(d, k) for d, k, _ in fetch] == [(d, k) for d, k, _ in write], "runs launched different kernels"
+    shard_bytes = w.n * w.Ht * w.d * 2
+    assert fetch[0][1].startswith("swap"), fetch[0][1]
+    fetch_scale = shard_bytes / (fetch[0][2] * 1024)
+    write_scale = shard_bytes / (write[0][2] * 1024)
+    doc = {
+        "workload": "%s head shard, one bench step (--steps 1 --warmup 0)" % workload,
+        "commands": [
+            "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $PMC -o fetch "
+            "-- python3 $REPO/bench.py --workload %s --steps 1 --warmup 0 --cpu-tokens 0" % workload,
+            "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $PMC -o write "
+            "-- python3 $REPO/bench.py --workload %s --steps 1 --warmup 0 --cpu-tokens 0" % workload,
+            "python3 $REPO/bench.py --workload %s --traffic-summary $PMC" % workload,
+        ],
+        "calibration": {
+            "kernel": "%s (a1 pack of the %d x %d x %d bf16 sequence shard: reads and writes exactly %d bytes)"
+                      % (fetch[0][1], w.n, w.Ht, w.d, shard_bytes),
+            "fetch_scale": fetch_scale,
+            "write_scale": write_scale,
+        },
+        "source_sha256": csrc_digest(),
+        "dispatches": [
+            {"dispatch": d, "kernel": k, "fetch_kb": fv, "write_kb": wv,
+             "hbm_bytes": int(round((fv * fetch_scale + wv * write_scale) * 1024))}
+            for (d, k, fv), (_, _, wv) in zip(fetch, write)
+        ],
+    }
+    out = os.path.join(ROOT, "profiles", "traffic_%s.txt" % workload)
+    with open(out, "w") as fh:
+        json.dump(doc, fh, indent=1)
+        fh.write("\n")
+    log("wrote %s" % out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,7 +177,12 @@ def main():
     ap.add_argument("--workload", default="64k", choices=["tiny", "8k", "64k", "varlen", "256k"])
     ap.add_argument("--cpu-tokens", type=int, default=9216,
                     help="tokens of the oracle's CPU-baseline sample (0 = skip)")
+    ap.add_argument("--traffic-summary", metavar="PMC_DIR",
+                    help="write profiles/traffic_<workload>.txt from two rocprofv3 counter runs and exit")
     args = ap.parse_args()
+    if args.traffic_summary:
+        write_traffic_summary(args.workload, args.traffic_summary)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU's share of the Ulysses path; runs on more than one GPU "

@@ -9,6 +9,11 @@
 // the token-split tensor and the chunk tensor, so the swap is a batch of
 // strided run copies. It is HBM-bound; each thread moves 16-byte vectors,
 // with several loads in flight before its stores.
+//
+// Two kernels: the token-major one (used whenever a token row fits its index
+// table) reads each token row front to back and scatters its vectors to the
+// P chunk runs; the run-major one copies one (chunk, segment) run per block
+// row and serves rows too long for the table.
 #include "uly_common.h"
 #include "uly_internal.h"
 
@@ -74,12 +79,112 @@ __global__ void __launch_bounds__(kSwapThreads) swap_kernel(SwapArgs a) {
   }
 }
 
+// Token-major kernel: a block copies kRowTokens whole token rows. For every
+// vector j of a token's chunk-ordered row (chunk p, local vector k) it looks
+// up the matching vector of the token-split row in a per-block LDS table, so
+// both sides are walked in long contiguous stretches. Loads and stores are
+// nontemporal: every byte is touched once. 512 threads x 4 vectors in flight
+// and 4 tokens per block measured best for a 12-KiB row.
+constexpr int kRowThreads = 512;
+constexpr int kRowTokens = 4;
+constexpr int kRowInFlight = 4;
+constexpr int kMaxRowVec = 4096;  // vectors per token row the table can hold
+
+struct RowArgs {
+  const u32x4 *src;
+  u32x4 *dst;
+  uint32_t n;         // tokens
+  uint32_t row_vec;   // vectors per token row (H*d/8)
+  uint32_t chunk_vec; // vectors per chunk row (h*d/8)
+  int nseg;
+  uint32_t seg_base_vec[8];   // segment start (vectors) in the token-split row
+  uint32_t seg_local_vec[8];  // vectors of one rank's block of the segment
+};
+
+template <bool kToHead>
+__global__ void __launch_bounds__(kRowThreads) swap_rows_kernel(RowArgs a) {
+  __shared__ uint32_t tab[kMaxRowVec];  // chunk-ordered index -> token-split index
+  for (uint32_t j = threadIdx.x; j < a.row_vec; j += kRowThreads) {
+    const uint32_t p = j / a.chunk_vec, k = j - p * a.chunk_vec;
+    uint32_t kk = k, src = 0;
+    for (int sgi = 0; sgi < a.nseg; ++sgi) {
+      const uint32_t L = a.seg_local_vec[sgi];
+      if (kk < L) {
+        src = a.seg_base_vec[sgi] + p * L + kk;
+        break;
+      }
+      kk -= L;
+    }
+    tab[j] = src;
+  }
+  __syncthreads();
+  const uint32_t t0 = blockIdx.x * kRowTokens;
+  const uint32_t nt = (a.n - t0) < (uint32_t)kRowTokens ? (a.n - t0) : (uint32_t)kRowTokens;
+  const uint32_t total = nt * a.row_vec;
+  constexpr int U = kRowInFlight;
+  for (uint32_t base = threadIdx.x; base < total; base += kRowThreads * U) {
+    u32x4 v[U];
+    int64_t di[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t i = base + u * kRowThreads;
+      di[u] = -1;
+      if (i < total) {
+        const uint32_t tl = i / a.row_vec;  // token within the block
+        const uint32_t j = i - tl * a.row_vec;
+        const uint32_t t = t0 + tl;
+        const uint32_t p = j / a.chunk_vec;
+        const int64_t c_idx = ((int64_t)p * a.n + t) * a.chunk_vec + (j - p * a.chunk_vec);
+        const int64_t s_idx = (int64_t)t * a.row_vec + tab[j];
+        if (kToHead) {
+          v[u] = __builtin_nontemporal_load(a.src + s_idx);
+          di[u] = c_idx;
+        } else {
+          v[u] = __builtin_nontemporal_load(a.src + c_idx);
+          di[u] = s_idx;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (di[u] >= 0) __builtin_nontemporal_store(v[u], a.dst + di[u]);
+  }
+}
+
 }  // namespace
+
+static int launch_swap_rows(bool to_head, const bf16_t *src, bf16_t *dst, int64_t n, int P, int nseg,
+                     const int32_t *seg_heads, int d, hipStream_t stream) {
+  RowArgs a;
+  a.src = reinterpret_cast<const u32x4 *>(src);
+  a.dst = reinterpret_cast<u32x4 *>(dst);
+  a.n = (uint32_t)n;
+  int64_t H = 0;
+  for (int s = 0; s < nseg; ++s) H += seg_heads[s];
+  a.row_vec = (uint32_t)(H * d / 8);
+  a.chunk_vec = (uint32_t)(H / P * d / 8);
+  a.nseg = nseg;
+  uint32_t base = 0;
+  for (int s = 0; s < 8; ++s) {
+    a.seg_base_vec[s] = s < nseg ? base : 0;
+    a.seg_local_vec[s] = s < nseg ? (uint32_t)(seg_heads[s] / P * d / 8) : 0;
+    if (s < nseg) base += (uint32_t)(seg_heads[s] * d / 8);
+  }
+  const unsigned blocks = (unsigned)((n + kRowTokens - 1) / kRowTokens);
+  if (to_head)
+    hipLaunchKernelGGL(swap_rows_kernel<true>, dim3(blocks), dim3(kRowThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(swap_rows_kernel<false>, dim3(blocks), dim3(kRowThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_hip_error(e, "swap_rows_kernel");
+  return 0;
+}
 
 int launch_swap(bool to_head, const bf16_t *src, bf16_t *dst, int64_t n, int P, int nseg,
                 const int32_t *seg_heads, int d, hipStream_t stream) {
   int64_t H = 0;
   for (int s = 0; s < nseg; ++s) H += seg_heads[s];
+  if (H * d / 8 <= kMaxRowVec) return launch_swap_rows(to_head, src, dst, n, P, nseg, seg_heads, d, stream);
   const int64_t h = H / P;
   const int nruns = P * nseg;
   // Launch rows: at most kMaxSwapRuns (chunk, segment) runs per launch.

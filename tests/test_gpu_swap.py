@@ -37,6 +37,10 @@ def _unpack(r_bits, P, segs):
     (5, 3, [3, 6], 8),
     (11, 8, [8], 24),
     (50, 1, [4, 2, 2], 16),
+    # token rows of 6144 and 4096 16-byte vectors: just past and at the
+    # token-major kernel's index-table limit
+    (37, 4, [256, 64, 64], 128),
+    (9, 8, [128, 64, 64], 128),
 ])
 def test_swap_small_shapes_bit_exact(n, P, segs, d):
     x = workloads.normal_bf16((n, sum(segs), d), seed=n * 131 + P)
