@@ -24,6 +24,8 @@
 //      (2-stage ring; concurrent workgroups walk the same tiles in step):
 //      S = Q K^T, dP = dO V^T (K, V in registers; a lane owns one key),
 //      P, dS, dV^T += dO^T P, dK^T += Q^T dS.
+#include <type_traits>
+
 #include "attn_common.h"
 #include "uly_internal.h"
 
@@ -256,32 +258,45 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_bwd_dq_kernel(BwdArgs a
 
 // ---------------------------------------------------------- dkdv kernel ----
 
-template <int D, int NWK>
+template <int D>
 struct DkvCfg {
-  static constexpr int NT = NWK * 64;
-  static constexpr int BNK = 32 * NWK;  // keys per workgroup
+  static constexpr int NKB = 4;         // 32-key blocks per workgroup
+  static constexpr int NW = 2 * NKB;    // two waves per key block
+  static constexpr int NT = NW * 64;
+  static constexpr int BNK = 32 * NKB;  // keys per workgroup
   static constexpr int BQ = 64;         // queries per tile
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int TILE = BQ * D;
   static constexpr int NI = TILE / 512;  // 1 KiB copies per tile and tensor
-  static_assert(NI % NWK == 0, "copies must split evenly over the waves");
+  static_assert(NI % NW == 0, "copies must split evenly over the waves");
 };
 
-template <int D, int NWK>
-__global__ void __launch_bounds__(NWK * 64, 1) attn_bwd_dkdv_kernel(BwdArgs a) {
-  using C = DkvCfg<D, NWK>;
+// Waves w and w + NKB share key block w % NKB and split the work of a tile:
+//   wave w       (S role):  S = Q K^T, P = exp(S - LSE), dV^T += dO^T P
+//   wave w + NKB (dP role): dP = dO V^T, dS = P (dP - D), dK^T += Q^T dS
+// The S-role wave hands P (bf16, in MFMA operand order) to its partner
+// through LDS; dS is formed from that same rounded P, which is the P the
+// dV product uses. Each wave then holds one of K or V and one of the dK or
+// dV accumulators, so a wave fits in 256 registers and two waves share each
+// SIMD: one's MFMAs run while the other computes exponentials or dS.
+template <int D>
+__global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs a) {
+  using C = DkvCfg<D>;
   __shared__ __align__(16) bf16_t q0s[C::TILE], q1s[C::TILE];    // Q row tiles
   __shared__ __align__(16) bf16_t d0s[C::TILE], d1s[C::TILE];    // dO row tiles
   __shared__ __align__(16) bf16_t qt0[C::TILE], qt1[C::TILE];    // Q^T trans tiles
   __shared__ __align__(16) bf16_t dt0[C::TILE], dt1[C::TILE];    // dO^T trans tiles
   __shared__ __align__(16) float ls0[2 * C::BQ], ls1[2 * C::BQ];  // LSE*log2e, D
+  __shared__ __align__(16) bf16_t xp[C::NKB * 4 * 512];          // P hand-over
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31;
   const int hi32 = lane >> 5;
+  const int kbw = w % C::NKB;        // this wave's 32-key block
+  const bool srole = w < C::NKB;     // S role (else dP role)
 
   // Heaviest key blocks (earliest keys under the causal mask) first;
   // consecutive ids alternate KV heads.
@@ -290,7 +305,7 @@ __global__ void __launch_bounds__(NWK * 64, 1) attn_bwd_dkdv_kernel(BwdArgs a) {
   const int kb = item / a.hkv;
   const int64_t k0 = (int64_t)kb * C::BNK;
   const int64_t k_last = (k0 + C::BNK < a.N ? k0 + C::BNK : a.N) - 1;
-  const int64_t kw0 = k0 + (int64_t)w * 32;
+  const int64_t kw0 = k0 + (int64_t)kbw * 32;
   const bool wave_valid = kw0 < a.N;
   const int64_t kw_last = (kw0 + 32 < a.N ? kw0 + 32 : a.N) - 1;
 
@@ -310,28 +325,22 @@ __global__ void __launch_bounds__(NWK * 64, 1) attn_bwd_dkdv_kernel(BwdArgs a) {
     qhi = qr.hi;
   }
 
-  // K and V rows of this lane's key as B operands (B[k = d][n = key]).
-  bf16x8 kf[C::KS], vf[C::KS];
+  // K (S role) or V (dP role) row of this lane's key as B operand (B[k = d][n = key]).
+  const bf16_t *kv = srole ? a.k : a.v;
+  const int64_t kv_stride = srole ? a.k_stride : a.v_stride;
+  bf16x8 xf[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) {
-    u32x4 vk = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-    if (key_ok) {
-      const int64_t col = (int64_t)g * D + ks * 16 + hi32 * 8;
-      vk = *reinterpret_cast<const u32x4 *>(a.k + key * a.k_stride + col);
-      vv = *reinterpret_cast<const u32x4 *>(a.v + key * a.v_stride + col);
-    }
-    kf[ks] = as_bf16x8(vk);
-    vf[ks] = as_bf16x8(vv);
+    u32x4 x = {0, 0, 0, 0};
+    if (key_ok) x = *reinterpret_cast<const u32x4 *>(kv + key * kv_stride + (int64_t)g * D + ks * 16 + hi32 * 8);
+    xf[ks] = as_bf16x8(x);
   }
 
-  f32x16 acc_dk[C::DB], acc_dv[C::DB];
+  f32x16 acc[C::DB];  // dV^T (S role) or dK^T (dP role), [d][key]
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      acc_dk[db][i] = 0.f;
-      acc_dv[db][i] = 0.f;
-    }
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
   const int qt0_ = (int)(qr_lo / C::BQ);
   const int qt1_ = (int)((qr_hi + C::BQ - 1) / C::BQ);
@@ -341,10 +350,10 @@ __global__ void __launch_bounds__(NWK * 64, 1) attn_bwd_dkdv_kernel(BwdArgs a) {
   // Per-lane byte offsets of this wave's 16-byte slots inside a tile: row
   // tiles of Q and dO (token stride), trans tiles of Q^T and dO^T.
   const uint32_t qsb = (uint32_t)(a.q_stride * 2), dsb = (uint32_t)(a.do_stride * 2);
-  uint32_t qoff[C::NI / NWK], doff[C::NI / NWK], toff[C::NI / NWK];
+  uint32_t qoff[C::NI / C::NW], doff[C::NI / C::NW], toff[C::NI / C::NW];
 #pragma unroll
-  for (int i = 0; i < C::NI / NWK; ++i) {
-    const int s = (w + i * NWK) * 64 + lane;
+  for (int i = 0; i < C::NI / C::NW; ++i) {
+    const int s = (w + i * C::NW) * 64 + lane;
     const int r = s / (D / 8);
     const uint32_t cb = ((s % (D / 8)) ^ row_swz<D>(r)) << 4;
     qoff[i] = r * qsb + cb;
@@ -359,136 +368,196 @@ __global__ void __launch_bounds__(NWK * 64, 1) attn_bwd_dkdv_kernel(BwdArgs a) {
   auto tile_head = [&](int t) { return g * a.G + t % a.G; };
   auto tile_u0 = [&](int t) { return (uint32_t)(qt1_ - 1 - t / a.G) * C::BQ; };
 
-  auto issue = [&](int t, bf16_t *qs, bf16_t *ds, bf16_t *qts, bf16_t *dts, float *ls) {
+  // Copies of tile t: Q and dO row tiles, the dO^T trans tile and the
+  // tile's LSE*log2e and D (issue_rows); the Q^T trans tile (issue_qt),
+  // which is needed one tile later than the others (see the schedule below).
+  auto issue_rows = [&](int t, bf16_t *qs, bf16_t *ds, bf16_t *dts, float *ls) {
     const int h = tile_head(t);
     const uint32_t u0 = tile_u0(t);
     // Q and dO rows of head h (rows >= N read as zeros; they are masked).
     const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.q + (int64_t)h * D, head_rows_bytes(a.N, a.q_stride, D));
     const __amdgpu_buffer_rsrc_t drs =
         make_rsrc(a.dout + (int64_t)h * D, head_rows_bytes(a.N, a.do_stride, D));
-    const __amdgpu_buffer_rsrc_t qtr = make_rsrc(a.qt + (int64_t)h * D * a.Np, (uint32_t)(D * a.Np * 2));
     const __amdgpu_buffer_rsrc_t dtr = make_rsrc(a.dot + (int64_t)h * D * a.Np, (uint32_t)(D * a.Np * 2));
 #pragma unroll
-    for (int i = 0; i < C::NI / NWK; ++i) {
-      const int u = w + i * NWK;
+    for (int i = 0; i < C::NI / C::NW; ++i) {
+      const int u = w + i * C::NW;
       dma16(qrs, qoff[i] + u0 * qsb, 0, lds_ptr(qs + u * 512));
       dma16(drs, doff[i] + u0 * dsb, 0, lds_ptr(ds + u * 512));
-      dma16(qtr, toff[i], u0 * 2, lds_ptr(qts + u * 512));
       dma16(dtr, toff[i], u0 * 2, lds_ptr(dts + u * 512));
     }
-    if (w < 2) {  // wave 0: LSE*log2e of the 64 rows, wave 1: D (padded rows, masked)
+    if (w < 2) {  // wave 0: LSE*log2e of the 64 rows, wave 1: D; rows >= N read as zeros
       const float *src = (w == 0 ? a.lse2 : a.delta) + (int64_t)h * a.Np;
-      dma4(make_rsrc(src, (uint32_t)(a.Np * 4)), lane * 4, u0 * 4, lds_ptr(ls + w * C::BQ));
+      dma4(make_rsrc(src, (uint32_t)(a.N * 4)), (u0 + lane) * 4, 0, lds_ptr(ls + w * C::BQ));
     }
   };
-
-  auto compute = [&](int t, const bf16_t *qs, const bf16_t *ds, const bf16_t *qts, const bf16_t *dts,
-                     const float *ls) {
+  auto issue_qt = [&](int t, bf16_t *qts) {
+    const int h = tile_head(t);
+    const uint32_t u0 = tile_u0(t);
+    const __amdgpu_buffer_rsrc_t qtr = make_rsrc(a.qt + (int64_t)h * D * a.Np, (uint32_t)(D * a.Np * 2));
+#pragma unroll
+    for (int i = 0; i < C::NI / C::NW; ++i) dma16(qtr, toff[i], u0 * 2, lds_ptr(qts + (w + i * C::NW) * 512));
+  };
+  auto active = [&](int t) {
     const int64_t u0 = tile_u0(t);
-    if (!(wave_valid && u0 < w_hi && u0 + C::BQ > w_lo)) return;
-    const bool need_mask = (u0 < w_lo_max) || (u0 + C::BQ > w_hi_min);
-    {
-      constexpr int QB0 = 0, QBN = 2;  // both 32-query halves of the tile at once
-      f32x16 s[QBN], dp[QBN];
+    return wave_valid && u0 < w_hi && u0 + C::BQ > w_lo;
+  };
+
+  // Schedule of tile t (stage t % 2 of every ring; B = ring barrier, X = P
+  // hand-over barrier):
+  //   wait for tile t's copies (all but Q^T(t)), B, issue_rows(t + 1)
+  //   phase 1  S role:  S(t), P(t), P -> LDS
+  //            dP role: dK += Q^T(t-1) dS(t-1), dP(t)
+  //   X, issue_qt(t + 1) (its stage held Q^T(t-1), last read in phase 1)
+  //   phase 2  S role:  dV += dO^T(t) P(t)
+  //            dP role: P(t) <- LDS, dS(t) (kept in registers for tile t+1)
+  // Each phase pairs one wave's exponentials or dS arithmetic with its
+  // partner's MFMAs on the same SIMD.
+  auto run = [&](auto role) __attribute__((always_inline)) {
+    constexpr bool S = decltype(role)::value;
+    bf16_t *xw = xp + kbw * 4 * 512 + lane * 8;  // this lane's 4 fragments, 1 KiB apart
+    bf16x8 sf[4];                                 // dP role: dS of the previous tile
+    bool pend = false;                            // dP role: sf holds a tile not yet applied
+
+    auto dk_update = [&](const bf16_t *qts) __attribute__((always_inline)) {
 #pragma unroll
-    for (int qi_ = 0; qi_ < QBN; ++qi_)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s[qi_][i] = 0.f;
-        dp[qi_][i] = 0.f;
-      }
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-#pragma unroll
-      for (int qi_ = 0; qi_ < QBN; ++qi_) {
-        const int qb2 = QB0 + qi_;
-        const int off = rt_off<D>(qb2 * 32 + l32, ks * 2 + hi32);
-        const bf16x8 aq = as_bf16x8(*reinterpret_cast<const u32x4 *>(qs + off));
-        const bf16x8 ad = as_bf16x8(*reinterpret_cast<const u32x4 *>(ds + off));
-        s[qi_] = mfma32(aq, kf[ks], s[qi_]);
-        dp[qi_] = mfma32(ad, vf[ks], dp[qi_]);
-      }
-    }
-#pragma unroll
-    for (int qi_ = 0; qi_ < QBN; ++qi_) {
-      const int qb2 = QB0 + qi_;
-      if (need_mask) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int64_t qi = u0 + qb2 * 32 + (i >> 2) * 8 + hi32 * 4 + (i & 3);
-          if (qi < qlo || qi >= qhi) s[qi_][i] = -INFINITY;
-        }
-      }
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int qo = qb2 * 32 + gq * 8 + hi32 * 4;
-        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(ls + qo);
-        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(ls + C::BQ + qo);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = gq * 4 + e;
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[qi_][i], a.c, -l4[e]));
-          s[qi_][i] = p;
-          dp[qi_][i] = p * (dp[qi_][i] - d4[e]);  // dS
-        }
-      }
-    }
-#pragma unroll
-    for (int qi_ = 0; qi_ < QBN; ++qi_) {
-      const int qb2 = QB0 + qi_;
-#pragma unroll
-      for (int jq = 0; jq < 2; ++jq) {
-        const int b = jq * 8;
-        const f32x16 &pv = s[qi_];
-        const f32x16 &sv = dp[qi_];
-        const bf16x8 pf = cvt8(pv[b + 0], pv[b + 1], pv[b + 2], pv[b + 3], pv[b + 4], pv[b + 5], pv[b + 6],
-                               pv[b + 7]);
-        const bf16x8 sf = cvt8(sv[b + 0], sv[b + 1], sv[b + 2], sv[b + 3], sv[b + 4], sv[b + 5], sv[b + 6],
-                               sv[b + 7]);
+      for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-          const int off = tr_off(db * 32 + l32, qb2 * 4 + jq * 2 + hi32);
-          const bf16x8 adt = as_bf16x8(*reinterpret_cast<const u32x4 *>(dts + off));
-          const bf16x8 aqt = as_bf16x8(*reinterpret_cast<const u32x4 *>(qts + off));
-          acc_dv[db] = mfma32(adt, pf, acc_dv[db]);
-          acc_dk[db] = mfma32(aqt, sf, acc_dk[db]);
+          const bf16x8 aqt = as_bf16x8(*reinterpret_cast<const u32x4 *>(qts + tr_off(db * 32 + l32, c * 2 + hi32)));
+          acc[db] = mfma32(aqt, sf[c], acc[db]);
+        }
+    };
+
+    auto tile = [&](int t, const bf16_t *qs, const bf16_t *ds, const bf16_t *dts, const float *ls,
+                    const bf16_t *qts_prev, bf16_t *qs_n, bf16_t *ds_n, bf16_t *dts_n, float *ls_n,
+                    bf16_t *qts_n) __attribute__((always_inline)) {
+      wait_vmcnt<C::NI / C::NW>();
+      barrier();
+      if (t + 1 < ntiles) issue_rows(t + 1, qs_n, ds_n, dts_n, ls_n);
+      const int64_t u0 = tile_u0(t);
+      const bool act = active(t);
+      f32x16 x[2];
+      bf16x8 pf[4];
+      if constexpr (!S) {
+        if (pend) dk_update(qts_prev);
+      }
+      if (act) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) x[q][i] = 0.f;
+        const bf16_t *rows = S ? qs : ds;
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const bf16x8 ar =
+                as_bf16x8(*reinterpret_cast<const u32x4 *>(rows + rt_off<D>(q * 32 + l32, ks * 2 + hi32)));
+            x[q] = mfma32(ar, xf[ks], x[q]);
+          }
+        if constexpr (S) {
+          if ((u0 < w_lo_max) || (u0 + C::BQ > w_hi_min)) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int64_t qi = u0 + q * 32 + (i >> 2) * 8 + hi32 * 4 + (i & 3);
+                if (qi < qlo || qi >= qhi) x[q][i] = -INFINITY;
+              }
+          }
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const f32x4 l4 = *reinterpret_cast<const f32x4 *>(ls + q * 32 + gq * 8 + hi32 * 4);
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                x[q][gq * 4 + e] = __builtin_amdgcn_exp2f(fmaf(x[q][gq * 4 + e], a.c, -l4[e]));
+            }
+#pragma unroll
+            for (int jq = 0; jq < 2; ++jq) {
+              const int b = jq * 8;
+              pf[q * 2 + jq] = cvt8(x[q][b + 0], x[q][b + 1], x[q][b + 2], x[q][b + 3], x[q][b + 4],
+                                    x[q][b + 5], x[q][b + 6], x[q][b + 7]);
+              *reinterpret_cast<bf16x8 *>(xw + (q * 2 + jq) * 512) = pf[q * 2 + jq];
+            }
+          }
         }
       }
-    }
-    }
-  };
+      lds_barrier();
+      if (t + 1 < ntiles) issue_qt(t + 1, qts_n);
+      if constexpr (S) {
+        if (act) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db) {
+              const bf16x8 adt =
+                  as_bf16x8(*reinterpret_cast<const u32x4 *>(dts + tr_off(db * 32 + l32, c * 2 + hi32)));
+              acc[db] = mfma32(adt, pf[c], acc[db]);
+            }
+        }
+      } else {
+        pend = act;
+        if (act) {
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int jq = 0; jq < 2; ++jq) {
+              const u32x4 pw = *reinterpret_cast<const u32x4 *>(xw + (q * 2 + jq) * 512);
+              float dsv[8];
+#pragma unroll
+              for (int gq2 = 0; gq2 < 2; ++gq2) {
+                const int gq = jq * 2 + gq2;
+                const f32x4 d4 = *reinterpret_cast<const f32x4 *>(ls + C::BQ + q * 32 + gq * 8 + hi32 * 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const int k = gq2 * 4 + e;  // fragment element
+                  const uint32_t wd = pw[k >> 1];
+                  const float p = __uint_as_float((k & 1) ? (wd & 0xFFFF0000u) : (wd << 16));
+                  dsv[k] = p * (x[q][gq * 4 + e] - d4[e]);
+                }
+              }
+              sf[q * 2 + jq] = cvt8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+            }
+        }
+      }
+    };
 
-  // Two stages: wait for tile t, barrier (tile t complete, the other stage
-  // free), prefetch t+1 into the other stage, compute t.
-  if (ntiles > 0) issue(0, q0s, d0s, qt0, dt0, ls0);
-  for (int t = 0; t < ntiles; t += 2) {
+    if (ntiles > 0) {
+      issue_rows(0, q0s, d0s, dt0, ls0);
+      issue_qt(0, qt0);
+    }
+    for (int t = 0; t < ntiles; t += 2) {
+      tile(t, q0s, d0s, dt0, ls0, qt1, q1s, d1s, dt1, ls1, qt1);
+      if (t + 1 < ntiles) tile(t + 1, q1s, d1s, dt1, ls1, qt0, q0s, d0s, dt0, ls0, qt0);
+    }
+    // The last tile's dK update: its Q^T copy is complete once every wave
+    // has waited for its own part of it.
     wait_vmcnt<0>();
     barrier();
-    if (t + 1 < ntiles) issue(t + 1, q1s, d1s, qt1, dt1, ls1);
-    compute(t, q0s, d0s, qt0, dt0, ls0);
-    if (t + 1 < ntiles) {
-      wait_vmcnt<0>();
-      barrier();
-      if (t + 2 < ntiles) issue(t + 2, q0s, d0s, qt0, dt0, ls0);
-      compute(t + 1, q1s, d1s, qt1, dt1, ls1);
+    if constexpr (!S) {
+      if (pend) dk_update((ntiles - 1) % 2 == 0 ? qt0 : qt1);
     }
-  }
+  };
+  if (srole)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 
   if (key_ok) {
-    bf16_t *dko = a.dk + key * a.dk_stride + (int64_t)g * D;
-    bf16_t *dvo = a.dv + key * a.dv_stride + (int64_t)g * D;
+    bf16_t *out = srole ? a.dv + key * a.dv_stride + (int64_t)g * D : a.dk + key * a.dk_stride + (int64_t)g * D;
+    const float f = srole ? 1.f : a.scale;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         const int d0 = db * 32 + gq * 8 + hi32 * 4;
-        u32x2 pk, pv2;
-        pk[0] = pack_bf16x2(acc_dk[db][gq * 4 + 0] * a.scale, acc_dk[db][gq * 4 + 1] * a.scale);
-        pk[1] = pack_bf16x2(acc_dk[db][gq * 4 + 2] * a.scale, acc_dk[db][gq * 4 + 3] * a.scale);
-        pv2[0] = pack_bf16x2(acc_dv[db][gq * 4 + 0], acc_dv[db][gq * 4 + 1]);
-        pv2[1] = pack_bf16x2(acc_dv[db][gq * 4 + 2], acc_dv[db][gq * 4 + 3]);
-        *reinterpret_cast<u32x2 *>(dko + d0) = pk;
-        *reinterpret_cast<u32x2 *>(dvo + d0) = pv2;
+        u32x2 pk;
+        pk[0] = pack_bf16x2(acc[db][gq * 4 + 0] * f, acc[db][gq * 4 + 1] * f);
+        pk[1] = pack_bf16x2(acc[db][gq * 4 + 2] * f, acc[db][gq * 4 + 3] * f);
+        *reinterpret_cast<u32x2 *>(out + d0) = pk;
       }
   }
 }
@@ -505,11 +574,11 @@ int launch_dq_cfg(BwdArgs a, hipStream_t stream) {
   return 0;
 }
 
-template <int D, int NWK>
+template <int D>
 int launch_dkdv_cfg(BwdArgs a, hipStream_t stream) {
-  using C = DkvCfg<D, NWK>;
+  using C = DkvCfg<D>;
   a.nblk = (int)((a.N + C::BNK - 1) / C::BNK);
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, NWK>), dim3((unsigned)((int64_t)a.nblk * a.hkv)),
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), dim3((unsigned)((int64_t)a.nblk * a.hkv)),
                      dim3(C::NT), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_hip_error(e, "attn_bwd_dkdv_kernel");
@@ -575,7 +644,7 @@ int launch_attn_bwd(const AttnShape &s, const AttnBwdPtrs &p, int parts, hipStre
                       : launch_dq_cfg<64, 1, 8>(a, stream);
     if (rc) return rc;
   }
-  if (parts & 2) rc = s.d == 128 ? launch_dkdv_cfg<128, 4>(a, stream) : launch_dkdv_cfg<64, 4>(a, stream);
+  if (parts & 2) rc = s.d == 128 ? launch_dkdv_cfg<128>(a, stream) : launch_dkdv_cfg<64>(a, stream);
   return rc;
 }
 

@@ -120,6 +120,16 @@ __device__ __forceinline__ void wait_vmcnt() {
 // direct-to-LDS copies are covered by the explicit vmcnt waits before it.
 __device__ __forceinline__ void barrier() { __builtin_amdgcn_s_barrier(); }
 
+// Workgroup barrier after this wave's own LDS stores (s_waitcnt lgkmcnt(0),
+// then s_barrier), without waiting for direct-to-LDS copies still in flight.
+// The empty asm statements keep the compiler from moving LDS accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
 // Value of lane l ^ 32.
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
