@@ -427,6 +427,7 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
           const bf16x8 aqt = as_bf16x8(*reinterpret_cast<const u32x4 *>(qts + tr_off(db * 32 + l32, c * 2 + hi32)));
           acc[db] = mfma32(aqt, sf[c], acc[db]);
         }
+      pipeline_reads_mfma<4 * C::DB>();
     };
 
     auto tile = [&](int t, const bf16_t *qs, const bf16_t *ds, const bf16_t *dts, const float *ls,
@@ -456,6 +457,7 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
                 as_bf16x8(*reinterpret_cast<const u32x4 *>(rows + rt_off<D>(q * 32 + l32, ks * 2 + hi32)));
             x[q] = mfma32(ar, xf[ks], x[q]);
           }
+        pipeline_reads_mfma<2 * C::KS>();
         if constexpr (S) {
           if ((u0 < w_lo_max) || (u0 + C::BQ > w_hi_min)) {
 #pragma unroll
@@ -497,6 +499,7 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
                   as_bf16x8(*reinterpret_cast<const u32x4 *>(dts + tr_off(db * 32 + l32, c * 2 + hi32)));
               acc[db] = mfma32(adt, pf[c], acc[db]);
             }
+          pipeline_reads_mfma<4 * C::DB>();
         }
       } else {
         pend = act;

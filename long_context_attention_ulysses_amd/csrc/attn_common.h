@@ -130,6 +130,21 @@ __device__ __forceinline__ void lds_barrier() {
   __asm__ volatile("" ::: "memory");
 }
 
+// Scheduling hint for the basic block it ends: LA LDS reads first, then
+// one MFMA and one LDS read alternately, then the last LA MFMAs, so that
+// each MFMA's operand was requested LA reads earlier (group masks: 0x100
+// LDS reads, 0x008 MFMA).
+template <int NR, int LA = 4>
+__device__ __forceinline__ void pipeline_reads_mfma() {
+  __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
+#pragma unroll
+  for (int i = 0; i < NR - LA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
+}
+
 // Value of lane l ^ 32.
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 

@@ -172,6 +172,7 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_fwd_kernel(FwdArgs a) {
         s[kb] = mfma32(af, qf[ks], s[kb]);
       }
     }
+    pipeline_reads_mfma<2 * C::KS>();
     if ((t0 < w_lo_max) || (t0 + C::BN > w_hi_min)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -231,6 +232,7 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_fwd_kernel(FwdArgs a) {
         acc_o[db] = mfma32(af, pf[j], acc_o[db]);
       }
     }
+    pipeline_reads_mfma<C::JS * C::DB>();
   };
 
   // Tile t lives in stage (t - kt0) % 3; at step t: wait for tile t, barrier
