@@ -171,55 +171,51 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_bwd_dq_kernel(BwdArgs a
     }
   };
 
+  // One 64-key tile, as two 32-key halves in turn (keeps one half's S^T and
+  // dP^T in registers at a time).
   auto compute = [&](int kt, const bf16_t *ks_, const bf16_t *vs_, const bf16_t *ts_) {
     const int64_t t0 = (int64_t)kt * C::BN;
     if (!(wave_valid && t0 < w_hi && t0 + C::BN > w_lo)) return;
-    f32x16 s[2], dp[2];
+    const bool need_mask = (t0 < w_lo_max) || (t0 + C::BN > w_hi_min);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s, dp;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        s[kb][i] = 0.f;
-        dp[kb][i] = 0.f;
+        s[i] = 0.f;
+        dp[i] = 0.f;
       }
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int ks = 0; ks < C::KS; ++ks) {
         const int off = rt_off<D>(kb * 32 + l32, ks * 2 + hi32);
         const bf16x8 ak = as_bf16x8(*reinterpret_cast<const u32x4 *>(ks_ + off));
         const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4 *>(vs_ + off));
-        s[kb] = mfma32(ak, qf[ks], s[kb]);
-        dp[kb] = mfma32(av, dof[ks], dp[kb]);
+        s = mfma32(ak, qf[ks], s);
+        dp = mfma32(av, dof[ks], dp);
       }
-    }
-    if ((t0 < w_lo_max) || (t0 + C::BN > w_hi_min)) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      if (need_mask) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int64_t key = t0 + kb * 32 + (i >> 2) * 8 + hi32 * 4 + (i & 3);
-          if (key < rlo || key >= rhi) s[kb][i] = -INFINITY;
+          if (key < rlo || key >= rhi) s[i] = -INFINITY;
         }
-    }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.c, -lse2));
-        s[kb][i] = p * (dp[kb][i] - delta);  // dS^T
       }
 #pragma unroll
-    for (int j = 0; j < C::JS; ++j) {
-      const f32x16 &sv = s[j >> 1];
-      const int b = (j & 1) * 8;
-      const bf16x8 dsf =
-          cvt8(sv[b + 0], sv[b + 1], sv[b + 2], sv[b + 3], sv[b + 4], sv[b + 5], sv[b + 6], sv[b + 7]);
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[i], a.c, -lse2));
+        s[i] = p * (dp[i] - delta);  // dS^T
+      }
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        const bf16x8 ak =
-            as_bf16x8(*reinterpret_cast<const u32x4 *>(ts_ + tr_off(db * 32 + l32, 2 * j + hi32)));
-        acc[db] = mfma32(ak, dsf, acc[db]);
+      for (int jj = 0; jj < 2; ++jj) {
+        const int j = kb * 2 + jj;
+        const int b = jj * 8;
+        const bf16x8 dsf = cvt8(s[b + 0], s[b + 1], s[b + 2], s[b + 3], s[b + 4], s[b + 5], s[b + 6], s[b + 7]);
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const bf16x8 ak =
+              as_bf16x8(*reinterpret_cast<const u32x4 *>(ts_ + tr_off(db * 32 + l32, 2 * j + hi32)));
+          acc[db] = mfma32(ak, dsf, acc[db]);
+        }
       }
     }
   };
