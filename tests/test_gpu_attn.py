@@ -84,6 +84,10 @@ SMALL = [
     (640, 4, 2, 128, True, [0, 1, 2, 100, 101, 350, 640], 0.5),
     (700, 2, 1, 64, False, [0, 64, 65, 300, 700], 1.0),
     (1536, 8, 2, 128, True, None, 0.5),
+    (64, 2, 2, 128, True, None, 0.5),                               # exactly one tile, G = 1
+    (65, 8, 1, 128, True, None, 0.5),                               # one row past a tile, G = 8
+    (129, 6, 2, 64, True, None, 1.0),                               # G = 3, d = 64
+    (200, 4, 1, 128, True, [0, 1, 2, 3, 67, 130, 131, 200], 0.5),  # one-token documents
 ]
 
 
@@ -293,6 +297,35 @@ def test_attention_argument_errors():
     assert e.value.name == "ULY_E_ALIAS"
     torch.cuda.synchronize()
     assert np.all(host(o) == 0xFFFF)
+
+
+def test_workspace_contents_do_not_matter():
+    """Both workspaces are scratch: filling them with 0xFF bytes (NaN as
+    float) before the calls changes no output bit. Ragged N leaves padded
+    rows in every per-row workspace array, which must never be read as data."""
+    for N, hq, hkv, d, cu in ((300, 4, 2, 128, None), (1000, 8, 2, 128, [0, 1, 333, 1000]),
+                              (77, 2, 1, 64, None)):
+        print("workspace N=%d hq=%d hkv=%d d=%d docs=%s" % (N, hq, hkv, d, cu), flush=True)
+        qkv = workloads.normal_bf16((N, hq + 2 * hkv, d), seed=N + 5, sigma=0.5)
+        dy = workloads.normal_bf16((N, hq, d), seed=N + 6)
+        r = Run(qkv, hq, hkv, 1 / np.sqrt(d), cu=None if cu is None else np.array(cu, dtype=np.int32))
+        outs = []
+        for fill in (0x00, 0xFF):
+            wsf = torch.full((uly.attn_fwd_workspace_bytes(N, hq, hkv, d),), fill, dtype=torch.uint8, device="cuda")
+            wsb = torch.full((uly.attn_bwd_workspace_bytes(N, hq, hkv, d),), fill, dtype=torch.uint8, device="cuda")
+            o = sentinel((N, hq, d))
+            lse = torch.full((hq, N), float("nan"), dtype=torch.float32, device="cuda")
+            uly.attn_fwd(r.q, r.k, r.v, o, lse, r.scale, True, r.cu_dev, r.max_seqlen, wsf)
+            dqkv = sentinel((N, hq + 2 * hkv, d))
+            dyd = dev(dy)
+            uly.attn_bwd(r.q, r.k, r.v, o, lse, dyd, dqkv[:, :hq], dqkv[:, hq:hq + hkv], dqkv[:, hq + hkv:],
+                         r.scale, True, wsb, r.cu_dev, r.max_seqlen)
+            torch.cuda.synchronize()
+            outs.append((host(o), lse.cpu().numpy(), host(dqkv)))
+        assert np.array_equal(outs[0][0], outs[1][0])
+        assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
+        assert np.array_equal(outs[0][2], outs[1][2])
+        assert np.all(np.isfinite(oracle.bf16_to_f64(outs[1][2])))
 
 
 def test_split_backward_equals_attn_bwd():
