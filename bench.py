@@ -60,10 +60,20 @@ def cpu_baseline(w, tokens: int):
     U = tokens * (tokens + 1) // 2
     flops = 14.0 * w.d * U * w.hq
     del np
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.num_threads(),
+        "cpu_model": cpu_model,
         "kind": "oracle",
         "sample": "fp64 oracle causal attention fwd+bwd over the first %d of %d tokens of the head shard "
                   "(%d q / %d kv heads, d=%d); %.1f s" % (tokens, w.N, w.hq, w.hkv, w.d, dt),
@@ -74,6 +84,40 @@ def cpu_baseline(w, tokens: int):
 
 KERNEL_OF = {"a3_attn_fwd": "attn_fwd_kernel", "a7a9_attn_bwd_dq": "attn_bwd_dq_kernel",
              "a8_attn_bwd_dkdv": "attn_bwd_dkdv_kernel"}
+
+
+def swap_cold_warm(uly, torch, x_seq, send, P, segments, reps=10):
+    """The a1 pack timed alone, outside the step: cold (a 512 MiB scratch
+    write between repetitions evicts the MALL) and warm (back to back),
+    medians of `reps`, with a device-to-device copy of the same bytes as the
+    achievable-copy reference. Bytes counted: one read + one write."""
+    import numpy as np
+    nbytes = 2 * x_seq.numel() * x_seq.element_size()
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flat_src = x_seq.view(-1)
+    flat_dst = send.view(-1)
+
+    def timed(fn, cold):
+        ts = []
+        for _ in range(reps):
+            if cold:
+                scratch.fill_(1)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = float(np.median(ts))
+        return {"ms": round(ms, 4), "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+
+    pack = lambda: uly.ulysses_seq_to_head(x_seq, send, P, segments)
+    copy = lambda: flat_dst.copy_(flat_src)
+    out = {"bytes": nbytes, "pack_cold": timed(pack, True), "pack_warm": timed(pack, False),
+           "d2d_copy_cold": timed(copy, True), "d2d_copy_warm": timed(copy, False)}
+    del scratch
+    return out
 
 
 def csrc_digest():
@@ -276,8 +320,11 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     log("timed %d steps: %.3f ms/step" % (args.steps, ms_per_step))
 
-    kern_ms = {nm: float(np.mean([events[s][i].elapsed_time(events[s][i + 1]) for s in range(args.steps)]))
-               for i, nm in enumerate(names)}
+    kern_all = {nm: [events[s][i].elapsed_time(events[s][i + 1]) for s in range(args.steps)]
+                for i, nm in enumerate(names)}
+    kern_ms = {nm: float(np.mean(v)) for nm, v in kern_all.items()}
+    kern_med = {nm: float(np.median(v)) for nm, v in kern_all.items()}
+    peak_mem = torch.cuda.max_memory_allocated()
     attn_ms = kern_ms["a3_attn_fwd"] + kern_ms["a7a9_attn_bwd_dq"] + kern_ms["a8_attn_bwd_dkdv"]
     swap_gbps = {nm: swap_bytes[nm] / (kern_ms[nm] * 1e-3) / 1e9 for nm in swap_bytes}
     dom = max(flops, key=lambda nm: kern_ms[nm])
@@ -317,12 +364,18 @@ def main():
         "value_frac_peak": round(value / BF16_PEAK_TFLOPS, 4),
         "tokens_per_s": round(w.N / (attn_ms * 1e-3), 1),
         "kernel_ms": {k_: round(v_, 4) for k_, v_ in kern_ms.items()},
+        "kernel_ms_median": {k_: round(v_, 4) for k_, v_ in kern_med.items()},
         "kernel_tflops": {k_: round(flops[k_] / (kern_ms[k_] * 1e-3) / 1e12, 2) for k_ in flops},
+        "fwd_tflops": round(4.0 * d * U * hq / (kern_ms["a3_attn_fwd"] * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(10.0 * d * U * hq / ((kern_ms["a7a9_attn_bwd_dq"] + kern_ms["a8_attn_bwd_dkdv"]) * 1e-3)
+                            / 1e12, 2),
         "swap_gbps": {k_: round(v_, 1) for k_, v_ in swap_gbps.items()},
         "swap_frac_hbm": {k_: round(v_ / HBM_PEAK_GBPS, 4) for k_, v_ in swap_gbps.items()},
         "counted_flop_per_step": total_flops,
+        "peak_device_bytes": peak_mem,
         "unmasked_pairs_per_head": U,
     }
+    result["swap_a1_alone"] = swap_cold_warm(uly, torch, x_seq, send, P, w.segments)
     if args.cpu_tokens > 0:
         log("cpu baseline: oracle on %d tokens ..." % args.cpu_tokens)
         result["cpu_baseline"] = cpu_baseline(w, min(args.cpu_tokens, w.N))

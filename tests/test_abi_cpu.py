@@ -127,3 +127,14 @@ def test_attn_varlen_and_bwd_validation():
     assert bwd(dq=A) == uly.CODE["ULY_E_ALIAS"]
     assert bwd(dk=W + (1 << 20)) == uly.CODE["ULY_E_ALIAS"]
     assert bwd(dv=0) == uly.CODE["ULY_E_NULL"]
+
+
+def test_workspaces_grow_linearly_with_n():
+    """O(N) memory: no N x N buffer anywhere; the only device memory the
+    attention calls use beyond their inputs and outputs is the workspace."""
+    for hq, hkv, d in ((8, 2, 128), (4, 1, 64)):
+        for N in (4096, 65536, 262144):
+            f1, f2 = L.attn_fwd_workspace_bytes(N, hq, hkv, d), L.attn_fwd_workspace_bytes(2 * N, hq, hkv, d)
+            b1, b2 = L.attn_bwd_workspace_bytes(N, hq, hkv, d, 1), L.attn_bwd_workspace_bytes(2 * N, hq, hkv, d, 1)
+            assert f2 == 2 * f1 and abs(b2 - 2 * b1) <= 2048
+            assert b1 <= N * (2 * hq * 4 + (hkv + 2 * hq) * d * 2) + 2048
