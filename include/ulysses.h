@@ -219,6 +219,52 @@ int attn_bwd_dkdv(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
                   int32_t causal, const int32_t *cu_seqlens, int32_t n_seqs, const void *ws,
                   size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Ring attention, the variant the pages set against Ulysses ("Sequence
+ * Parallelism for Long-Context AI Training", "Advanced Scaling: Ring
+ * Attention and Ulysses": each GPU keeps the queries of its S/P tokens and
+ * computes local attention against the key/value block it holds while the
+ * blocks travel around a ring; "Ulysses Sequence Parallelism for
+ * Million-Token Context Training", "Comparing Ulysses and Ring Attention").
+ *
+ * One ring step on rank r is attn_fwd of its queries against the block of
+ * rank b, with causal != 0 for b == r and causal == 0 for b < r (blocks of
+ * later ranks are all masked and skipped). Each step's (o_j, lse_j) is the
+ * softmax over that block's keys only; attn_lse_merge combines them into
+ * attention over all keys:
+ *   lse = log sum_j exp(lse_j),  o = sum_j exp(lse_j - lse) o_j.
+ *
+ * o_parts:   host array of n_parts device pointers, each [N] rows of h heads
+ *            x d bf16 with token stride part_stride (elements).
+ * lse_parts: host array of n_parts device pointers, each [h][N] float32
+ *            (natural log, as attn_fwd writes it).
+ * o_out [N] rows of h x d bf16 (token stride out_stride), lse_out [h][N].
+ * n_parts: 1..16. A part whose lse is -inf for a row adds nothing to it; a
+ * row that is -inf in every part gets o = 0 and lse = -inf.
+ * d: a multiple of 8. Outputs may not overlap any part (no in-place merge).
+ * Errors: ULY_E_NULL, ULY_E_SHAPE (n_parts, N, h or d out of range),
+ * ULY_E_STRIDE, ULY_E_ALIGN (o pointers, strides or d; lse pointers need 4
+ * bytes), ULY_E_ALIAS, ULY_E_HIP.
+ */
+int attn_lse_merge(int32_t n_parts, const uint16_t *const *o_parts, const float *const *lse_parts,
+                   uint16_t *o_out, float *lse_out, int64_t N, int32_t h, int32_t d,
+                   int64_t part_stride, int64_t out_stride, hipStream_t stream);
+
+/*
+ * Backward of the ring: each step's attn_bwd, run with the merged o and lse
+ * (so that p and D are those of attention over all keys) and the step's
+ * causal flag, gives the block's share of dQ for the local queries and of dK
+ * and dV for the block's owner. ring_grad_sum adds such shares:
+ *   out = sum_j parts[j], accumulated in float32 and rounded to bf16 once.
+ * parts: host array of n_parts (1..16) device pointers, each [rows] x width
+ * bf16 with token stride part_stride; out [rows] x width, stride out_stride.
+ * width: a multiple of 8. out may not overlap any part.
+ * Errors: ULY_E_NULL, ULY_E_SHAPE, ULY_E_STRIDE, ULY_E_ALIGN, ULY_E_ALIAS,
+ * ULY_E_HIP.
+ */
+int ring_grad_sum(int32_t n_parts, const uint16_t *const *parts, uint16_t *out, int64_t rows,
+                  int32_t width, int64_t part_stride, int64_t out_stride, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

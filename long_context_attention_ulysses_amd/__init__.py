@@ -2,7 +2,10 @@
 
 The hot path (layout swaps around the all-to-all, causal GQA attention
 forward and backward, dense or packed documents) runs in libulysses.so,
-hand-written HIP for gfx950; this package is its thin Python binding.
+hand-written HIP for gfx950; this package is its thin Python binding. The
+same attention calls plus a merge of per-block results and a sum of
+per-block gradients also serve ring attention, the variant the pages
+contrast with Ulysses.
 """
 from ._lib import (  # noqa: F401
     EXPORTED,
@@ -16,7 +19,9 @@ from ._lib import (  # noqa: F401
     attn_bwd_workspace_bytes,
     attn_fwd,
     attn_fwd_workspace_bytes,
+    attn_lse_merge,
     raw,
+    ring_grad_sum,
     status_string,
     ulysses_check_cu_seqlens,
     ulysses_head_to_seq,

@@ -59,6 +59,9 @@ _SIGS = {
                     ctypes.c_int),
     "attn_bwd_dkdv": ([_p] * 7 + [_i64, _i32, _i32, _i32] + [_i64] * 6 + [_f32, _i32, _p, _i32, _p, _sz, _p],
                       ctypes.c_int),
+    "attn_lse_merge": ([_i32, ctypes.POINTER(_p), ctypes.POINTER(_p), _p, _p, _i64, _i32, _i32, _i64, _i64, _p],
+                       ctypes.c_int),
+    "ring_grad_sum": ([_i32, ctypes.POINTER(_p), _p, _i64, _i32, _i64, _i64, _p], ctypes.c_int),
 }
 for _name, (_args, _res) in _SIGS.items():
     _f = getattr(_L, _name)
@@ -216,3 +219,35 @@ def attn_bwd_dkdv(q, k, v, lse, dout, dk, dv, scale: float, causal: bool = True,
                             _tok_stride(dout, hq, d), _tok_stride(dk, hkv, d), _tok_stride(dv, hkv, d),
                             float(scale), int(bool(causal)), _ptr(cu_seqlens), n_seqs, _ptr(ws),
                             ws.numel() * ws.element_size(), _stream(stream)), "attn_bwd_dkdv")
+
+
+def _ptr_array(ts):
+    return (_p * len(ts))(*[t.data_ptr() for t in ts])
+
+
+def attn_lse_merge(o_parts, lse_parts, o_out, lse_out, stream=None) -> None:
+    """Merge per-block attention results (ring attention): o_parts are
+    [N, h, d] views with one common token stride, lse_parts [h, N] float32;
+    o_out [N, h, d], lse_out [h, N]."""
+    if len(o_parts) != len(lse_parts) or not o_parts:
+        raise ValueError("need as many lse parts as o parts, at least one")
+    N, h, d = o_out.shape
+    strides = {_tok_stride(t, h, d) for t in o_parts}
+    if len(strides) != 1 or any(tuple(t.shape) != (N, h, d) for t in o_parts):
+        raise ValueError("o parts must share one shape and token stride")
+    _check(_L.attn_lse_merge(len(o_parts), _ptr_array(o_parts), _ptr_array(lse_parts), _ptr(o_out),
+                             _ptr(lse_out), N, h, d, strides.pop(), _tok_stride(o_out, h, d), _stream(stream)),
+           "attn_lse_merge")
+
+
+def ring_grad_sum(parts, out, stream=None) -> None:
+    """out = sum of parts (bf16 [rows, heads, d] views with one common token
+    stride), accumulated in float32."""
+    if not parts:
+        raise ValueError("need at least one part")
+    rows, heads, d = out.shape
+    strides = {_tok_stride(t, heads, d) for t in parts}
+    if len(strides) != 1 or any(tuple(t.shape) != (rows, heads, d) for t in parts):
+        raise ValueError("parts must share one shape and token stride")
+    _check(_L.ring_grad_sum(len(parts), _ptr_array(parts), _ptr(out), rows, heads * d, strides.pop(),
+                            _tok_stride(out, heads, d), _stream(stream)), "ring_grad_sum")

@@ -338,3 +338,65 @@ int attn_bwd_dkdv(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
 }
 
 }  // extern "C"
+
+namespace uly {
+namespace {
+
+int check_parts(int32_t n_parts, const void *const *parts, int64_t rows, int64_t width,
+                int64_t part_stride) {
+  if (!parts) return ULY_E_NULL;
+  if (n_parts < 1 || n_parts > uly::kMaxParts) return ULY_E_SHAPE;
+  if (rows <= 0 || width <= 0) return ULY_E_SHAPE;
+  if (width % 8) return ULY_E_ALIGN;
+  if (rows * (width / 8) >= (int64_t)1 << 31) return ULY_E_SHAPE;  // 32-bit vector index
+  if (part_stride < width) return ULY_E_STRIDE;
+  if (part_stride % 8) return ULY_E_ALIGN;
+  for (int j = 0; j < n_parts; ++j) {
+    if (!parts[j]) return ULY_E_NULL;
+    if (!aligned16(parts[j])) return ULY_E_ALIGN;
+  }
+  return ULY_OK;
+}
+
+}  // namespace
+}  // namespace uly
+
+extern "C" int attn_lse_merge(int32_t n_parts, const uint16_t *const *o_parts,
+                              const float *const *lse_parts, uint16_t *o_out, float *lse_out,
+                              int64_t N, int32_t h, int32_t d, int64_t part_stride,
+                              int64_t out_stride, hipStream_t stream) {
+  using namespace uly;
+  if (!lse_parts || !o_out || !lse_out) return ULY_E_NULL;
+  if (h <= 0 || d <= 0) return ULY_E_SHAPE;
+  const int64_t width = (int64_t)h * d;
+  int rc = check_parts(n_parts, reinterpret_cast<const void *const *>(o_parts), N, width, part_stride);
+  if (rc) return rc;
+  if ((rc = check_out(o_out, N, out_stride, width))) return rc;
+  if (reinterpret_cast<uintptr_t>(lse_out) & 3u) return ULY_E_ALIGN;
+  const size_t ob = span_bytes(N, out_stride, width), lb = (size_t)N * h * 4;
+  if (overlaps(o_out, ob, lse_out, lb)) return ULY_E_ALIAS;
+  for (int j = 0; j < n_parts; ++j) {
+    if (!lse_parts[j]) return ULY_E_NULL;
+    if (reinterpret_cast<uintptr_t>(lse_parts[j]) & 3u) return ULY_E_ALIGN;
+    const size_t pb = span_bytes(N, part_stride, width);
+    if (overlaps(o_out, ob, o_parts[j], pb) || overlaps(o_out, ob, lse_parts[j], lb) ||
+        overlaps(lse_out, lb, o_parts[j], pb) || overlaps(lse_out, lb, lse_parts[j], lb))
+      return ULY_E_ALIAS;
+  }
+  return uly::launch_lse_merge(n_parts, o_parts, lse_parts, o_out, lse_out, N, h, d, part_stride,
+                               out_stride, stream);
+}
+
+extern "C" int ring_grad_sum(int32_t n_parts, const uint16_t *const *parts, uint16_t *out,
+                             int64_t rows, int32_t width, int64_t part_stride, int64_t out_stride,
+                             hipStream_t stream) {
+  using namespace uly;
+  if (!out) return ULY_E_NULL;
+  int rc = check_parts(n_parts, reinterpret_cast<const void *const *>(parts), rows, width, part_stride);
+  if (rc) return rc;
+  if ((rc = check_out(out, rows, out_stride, width))) return rc;
+  const size_t ob = span_bytes(rows, out_stride, width);
+  for (int j = 0; j < n_parts; ++j)
+    if (overlaps(out, ob, parts[j], span_bytes(rows, part_stride, width))) return ULY_E_ALIAS;
+  return uly::launch_grad_sum(n_parts, parts, out, rows, width, part_stride, out_stride, stream);
+}

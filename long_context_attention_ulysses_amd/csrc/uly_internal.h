@@ -76,4 +76,17 @@ struct AttnBwdPtrs {
 // parts: 1 = D and dQ, 2 = dK and dV (reads D), 3 = both in that order.
 int launch_attn_bwd(const AttnShape &s, const AttnBwdPtrs &p, int parts, hipStream_t stream);
 
+// Most per-block results one merge or gradient-sum launch takes.
+constexpr int kMaxParts = 16;
+
+// out, lse_out = merge of n_parts (o, lse) results over disjoint key blocks;
+// arguments validated.
+int launch_lse_merge(int n_parts, const bf16_t *const *o, const float *const *lse, bf16_t *out,
+                     float *lse_out, int64_t N, int h, int d, int64_t part_stride, int64_t out_stride,
+                     hipStream_t stream);
+
+// out = sum of n_parts bf16 [rows][width] views (float accumulation).
+int launch_grad_sum(int n_parts, const bf16_t *const *parts, bf16_t *out, int64_t rows, int width,
+                    int64_t part_stride, int64_t out_stride, hipStream_t stream);
+
 }  // namespace uly

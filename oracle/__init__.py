@@ -11,6 +11,8 @@ carries the citations):
   exchange                    the all-to-all itself, as buffer re-indexing
   attn_fwd                    softmax attention, causal and/or packed docs
   attn_bwd                    its textbook gradient
+  lse_merge                   ring attention: softmax over the union of
+                              disjoint key blocks from per-block results
 """
 from __future__ import annotations
 
@@ -168,3 +170,35 @@ def attn_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray, scal
     if rc != 0:
         raise RuntimeError("orc_attn_bwd failed: %d" % rc)
     return dq, dk, dv
+
+
+# ------------------------------------------------------------------ O4 ----
+
+def lse_merge(o_parts: Sequence[np.ndarray], lse_parts: Sequence[np.ndarray]
+              ) -> Tuple[np.ndarray, np.ndarray]:
+    """Ring attention ("Sequence Parallelism for Long-Context AI Training",
+    "Advanced Scaling: Ring Attention and Ulysses": each GPU attends its own
+    queries to one key/value block at a time as the blocks travel a ring).
+    Part j is attention over block j's keys only: o_j [N, h, d] and natural
+    log lse_j [h, N]. With the key blocks disjoint, the softmax over all of
+    them is, by the definition of softmax:
+        lse = log sum_j exp(lse_j)
+        o   = sum_j exp(lse_j - lse) o_j
+    (the max is taken out of the sum so that nothing overflows). A row that is
+    -inf in every part has no keys: o = 0, lse = -inf. fp64."""
+    L = [np.asarray(l, dtype=np.float64) for l in lse_parts]
+    O = [np.asarray(o, dtype=np.float64) for o in o_parts]
+    m = L[0].copy()
+    for l in L[1:]:
+        m = np.maximum(m, l)
+    empty = np.isneginf(m)
+    m_safe = np.where(empty, 0.0, m)
+    total = np.zeros_like(m)
+    for l in L:
+        total += np.exp(l - m_safe)
+    lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, total)))
+    o = np.zeros_like(O[0])
+    for l, oj in zip(L, O):
+        w = np.where(empty, 0.0, np.exp(l - np.where(empty, 0.0, lse)))  # [h, N]
+        o += w.T[:, :, None] * oj
+    return o, lse
