@@ -120,6 +120,70 @@ def swap_cold_warm(uly, torch, x_seq, send, P, segments, reps=10):
     return out
 
 
+def ring_step(uly, torch, w, x_seq, dy_seq, reps=3):
+    """Ring attention at the same sequence and P: rank P-1 (the one with the
+    most work) attends its n tokens x all Hq heads to all P key/value blocks
+    (its own block causal, the P-1 earlier ones unmasked), merges the P
+    results, then runs the P backward steps with the merged o and lse and sums
+    the P dQ shares. Every block reuses the rank's own q|k|v data (timing does
+    not depend on the values). Medians over `reps`."""
+    import numpy as np
+    P, n, Hq, Hkv, d = w.P, w.n, w.Hq, w.Hkv, w.d
+    q, k, v = x_seq[:, :Hq], x_seq[:, Hq:Hq + Hkv], x_seq[:, Hq + Hkv:]
+    o_parts = [torch.empty((n, Hq, d), dtype=torch.int16, device="cuda") for _ in range(P)]
+    l_parts = [torch.empty((Hq, n), dtype=torch.float32, device="cuda") for _ in range(P)]
+    o = torch.empty((n, Hq, d), dtype=torch.int16, device="cuda")
+    lse = torch.empty((Hq, n), dtype=torch.float32, device="cuda")
+    g_parts = [torch.empty((n, Hq + 2 * Hkv, d), dtype=torch.int16, device="cuda") for _ in range(P)]
+    dq = torch.empty((n, Hq, d), dtype=torch.int16, device="cuda")
+    wsf = torch.empty(uly.attn_fwd_workspace_bytes(n, Hq, Hkv, d), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(uly.attn_bwd_workspace_bytes(n, Hq, Hkv, d), dtype=torch.uint8, device="cuda")
+    causal = [b == P - 1 for b in range(P)]
+
+    def fwd():
+        for b in range(P):
+            uly.attn_fwd(q, k, v, o_parts[b], l_parts[b], w.scale, causal[b], None, None, wsf)
+
+    def merge():
+        uly.attn_lse_merge(o_parts, l_parts, o, lse)
+
+    def bwd():
+        for b in range(P):
+            g = g_parts[b]
+            uly.attn_bwd(q, k, v, o, lse, dy_seq, g[:, :Hq], g[:, Hq:Hq + Hkv], g[:, Hq + Hkv:], w.scale, causal[b],
+                         wsb)
+
+    def gsum():
+        uly.ring_grad_sum([g[:, :Hq] for g in g_parts], dq)
+
+    def timed(fn):
+        fn()
+        ts = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    t_fwd, t_merge, t_bwd, t_sum = timed(fwd), timed(merge), timed(bwd), timed(gsum)
+    pairs = (P - 1) * n * n + n * (n + 1) // 2  # per query head
+    merge_bytes = P * (n * Hq * d * 2 + Hq * n * 4) + n * Hq * d * 2 + Hq * n * 4
+    sum_bytes = (P + 1) * n * Hq * d * 2
+    return {
+        "rank": P - 1, "blocks": P, "tokens_per_block": n, "heads": [Hq, Hkv], "d": d,
+        "fwd_ms": round(t_fwd, 3), "fwd_tflops": round(4.0 * d * pairs * Hq / (t_fwd * 1e-3) / 1e12, 2),
+        "bwd_ms": round(t_bwd, 3), "bwd_tflops": round(10.0 * d * pairs * Hq / (t_bwd * 1e-3) / 1e12, 2),
+        "merge_ms": round(t_merge, 4), "merge_gbps": round(merge_bytes / (t_merge * 1e-3) / 1e9, 1),
+        "merge_frac_hbm": round(merge_bytes / (t_merge * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "grad_sum_ms": round(t_sum, 4), "grad_sum_gbps": round(sum_bytes / (t_sum * 1e-3) / 1e9, 1),
+        "grad_sum_frac_hbm": round(sum_bytes / (t_sum * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+    }
+
+
 def csrc_digest():
     """sha256 over the HIP sources (names and bytes), to tell whether stored
     counter readings still describe the kernels being run."""
@@ -221,6 +285,7 @@ def main():
     ap.add_argument("--workload", default="64k", choices=["tiny", "8k", "64k", "varlen", "256k"])
     ap.add_argument("--cpu-tokens", type=int, default=9216,
                     help="tokens of the oracle's CPU-baseline sample (0 = skip)")
+    ap.add_argument("--no-ring", action="store_true", help="skip the ring-attention measurement")
     ap.add_argument("--traffic-summary", metavar="PMC_DIR",
                     help="write profiles/traffic_<workload>.txt from two rocprofv3 counter runs and exit")
     args = ap.parse_args()
@@ -376,6 +441,9 @@ def main():
         "unmasked_pairs_per_head": U,
     }
     result["swap_a1_alone"] = swap_cold_warm(uly, torch, x_seq, send, P, w.segments)
+    if not args.no_ring and cu is None:
+        log("ring attention step (rank %d of %d) ..." % (P - 1, P))
+        result["ring"] = ring_step(uly, torch, w, x_seq, dy_seq)
     if args.cpu_tokens > 0:
         log("cpu baseline: oracle on %d tokens ..." % args.cpu_tokens)
         result["cpu_baseline"] = cpu_baseline(w, min(args.cpu_tokens, w.N))
