@@ -265,6 +265,50 @@ int attn_lse_merge(int32_t n_parts, const uint16_t *const *o_parts, const float 
 int ring_grad_sum(int32_t n_parts, const uint16_t *const *parts, uint16_t *out, int64_t rows,
                   int32_t width, int64_t part_stride, int64_t out_stride, hipStream_t stream);
 
+/*
+ * Loss of an SP step from pre-shifted labels ("Deepspeed Ulysses/ALST
+ * integration", opening post, step 2; "Ulysses sequence parallelism",
+ * Configure: the Trainer shifts labels and aggregates the loss across SP
+ * ranks). Each rank holds the logits of its own n tokens and their
+ * shift_labels (the label of token i is token i+1 of the full sequence; -100
+ * marks tokens without a loss, e.g. prompt tokens or the last token).
+ *
+ * shifted_ce_fwd, per rank: for every row r with a good label y_r (in
+ * [0, V)): row_loss[r] = lse_r - logit_{r,y_r} with lse_r = log sum_v
+ * exp(logit_rv) (natural log); row_loss = 0 for other labels. Then
+ * *loss_out = mean of row_loss over good rows (0 if there are none) and
+ * *good_out = their count, summed in a fixed order (deterministic).
+ *   logits [n] rows of V bf16, row stride `stride` elements (finite values);
+ *   labels [n] int32, device; row_loss, row_lse [n] float32 (outputs;
+ *   row_lse is kept for shifted_ce_bwd); loss_out, good_out: device scalars.
+ *   V: a multiple of 8.
+ *
+ * sp_loss_aggregate: the differentiable weighted aggregation across ranks,
+ *   *total_out = sum_r loss_r * good_r / max(sum_r good_r, 1),
+ * from n_ranks (1..16) device scalars (host arrays of device pointers), and
+ * *row_grad_scale_out = 1 / max(sum_r good_r, 1), the factor every good
+ * row's gradient carries.
+ *
+ * shifted_ce_bwd, per rank: the gradient of the aggregate with respect to
+ * the rank's logits: dlogits[r] = (softmax(logits[r]) - onehot(y_r)) *
+ * (*row_grad_scale) for good rows, 0 for the others. dlogits may be the
+ * logits buffer itself (same pointer and stride: each element is read before
+ * it is overwritten); any other overlap is ULY_E_ALIAS.
+ *
+ * Errors: ULY_E_NULL, ULY_E_SHAPE (n, V or n_ranks out of range), ULY_E_STRIDE,
+ * ULY_E_ALIGN (logits/dlogits 16-byte aligned, strides and V multiples of 8),
+ * ULY_E_ALIAS, ULY_E_HIP.
+ */
+int shifted_ce_fwd(const uint16_t *logits, const int32_t *labels, int64_t n, int64_t V,
+                   int64_t stride, float *row_loss, float *row_lse, float *loss_out,
+                   int32_t *good_out, hipStream_t stream);
+int sp_loss_aggregate(int32_t n_ranks, const float *const *rank_loss,
+                      const int32_t *const *rank_good, float *total_out, float *row_grad_scale_out,
+                      hipStream_t stream);
+int shifted_ce_bwd(const uint16_t *logits, const int32_t *labels, const float *row_lse,
+                   const float *row_grad_scale, int64_t n, int64_t V, int64_t stride,
+                   uint16_t *dlogits, int64_t dstride, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -5,7 +5,8 @@ forward and backward, dense or packed documents) runs in libulysses.so,
 hand-written HIP for gfx950; this package is its thin Python binding. The
 same attention calls plus a merge of per-block results and a sum of
 per-block gradients also serve ring attention, the variant the pages
-contrast with Ulysses.
+contrast with Ulysses; the shifted-label loss and its weighted aggregation
+over the SP ranks close the step.
 """
 from ._lib import (  # noqa: F401
     EXPORTED,
@@ -22,6 +23,9 @@ from ._lib import (  # noqa: F401
     attn_lse_merge,
     raw,
     ring_grad_sum,
+    shifted_ce_bwd,
+    shifted_ce_fwd,
+    sp_loss_aggregate,
     status_string,
     ulysses_check_cu_seqlens,
     ulysses_head_to_seq,

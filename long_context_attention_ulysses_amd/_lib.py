@@ -62,6 +62,9 @@ _SIGS = {
     "attn_lse_merge": ([_i32, ctypes.POINTER(_p), ctypes.POINTER(_p), _p, _p, _i64, _i32, _i32, _i64, _i64, _p],
                        ctypes.c_int),
     "ring_grad_sum": ([_i32, ctypes.POINTER(_p), _p, _i64, _i32, _i64, _i64, _p], ctypes.c_int),
+    "shifted_ce_fwd": ([_p, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p], ctypes.c_int),
+    "sp_loss_aggregate": ([_i32, ctypes.POINTER(_p), ctypes.POINTER(_p), _p, _p, _p], ctypes.c_int),
+    "shifted_ce_bwd": ([_p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _p], ctypes.c_int),
 }
 for _name, (_args, _res) in _SIGS.items():
     _f = getattr(_L, _name)
@@ -251,3 +254,36 @@ def ring_grad_sum(parts, out, stream=None) -> None:
         raise ValueError("parts must share one shape and token stride")
     _check(_L.ring_grad_sum(len(parts), _ptr_array(parts), _ptr(out), rows, heads * d, strides.pop(),
                             _tok_stride(out, heads, d), _stream(stream)), "ring_grad_sum")
+
+
+def _row_stride(t, V):
+    if t.dim() != 2 or t.shape[1] != V or t.stride(1) != 1:
+        raise ValueError("expected an [n, V] view with unit element stride")
+    return t.stride(0)
+
+
+def shifted_ce_fwd(logits, labels, row_loss, row_lse, loss_out, good_out, stream=None) -> None:
+    """Per-rank loss from pre-shifted labels: logits [n, V] bf16 bits,
+    labels [n] int32 (-100 = no loss); outputs row_loss, row_lse [n] float32,
+    loss_out [1] float32 (mean over good rows), good_out [1] int32."""
+    n, V = logits.shape
+    _check(_L.shifted_ce_fwd(_ptr(logits), _ptr(labels), n, V, _row_stride(logits, V), _ptr(row_loss),
+                             _ptr(row_lse), _ptr(loss_out), _ptr(good_out), _stream(stream)), "shifted_ce_fwd")
+
+
+def sp_loss_aggregate(rank_losses, rank_goods, total_out, row_grad_scale_out, stream=None) -> None:
+    """sum_r loss_r * good_r / max(sum_r good_r, 1) over the ranks' device
+    scalars, and the per-row gradient scale 1 / max(sum_r good_r, 1)."""
+    if len(rank_losses) != len(rank_goods) or not rank_losses:
+        raise ValueError("need one good count per rank loss, at least one rank")
+    _check(_L.sp_loss_aggregate(len(rank_losses), _ptr_array(rank_losses), _ptr_array(rank_goods),
+                                _ptr(total_out), _ptr(row_grad_scale_out), _stream(stream)), "sp_loss_aggregate")
+
+
+def shifted_ce_bwd(logits, labels, row_lse, row_grad_scale, dlogits, stream=None) -> None:
+    """Gradient of the aggregate loss with respect to one rank's logits
+    (dlogits may be logits itself)."""
+    n, V = logits.shape
+    _check(_L.shifted_ce_bwd(_ptr(logits), _ptr(labels), _ptr(row_lse), _ptr(row_grad_scale), n, V,
+                             _row_stride(logits, V), _ptr(dlogits), _row_stride(dlogits, V), _stream(stream)),
+           "shifted_ce_bwd")

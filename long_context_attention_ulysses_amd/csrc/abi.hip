@@ -400,3 +400,58 @@ extern "C" int ring_grad_sum(int32_t n_parts, const uint16_t *const *parts, uint
     if (overlaps(out, ob, parts[j], span_bytes(rows, part_stride, width))) return ULY_E_ALIAS;
   return uly::launch_grad_sum(n_parts, parts, out, rows, width, part_stride, out_stride, stream);
 }
+
+namespace uly {
+namespace {
+
+int check_logits(const void *logits, int64_t n, int64_t V, int64_t stride) {
+  if (!logits) return ULY_E_NULL;
+  if (n <= 0 || n >= ((int64_t)1 << 31) || V < 8 || V >= ((int64_t)1 << 31)) return ULY_E_SHAPE;
+  if (V % 8) return ULY_E_ALIGN;
+  if (stride < V) return ULY_E_STRIDE;
+  if (stride % 8 || !aligned16(logits)) return ULY_E_ALIGN;
+  return ULY_OK;
+}
+
+}  // namespace
+}  // namespace uly
+
+extern "C" int shifted_ce_fwd(const uint16_t *logits, const int32_t *labels, int64_t n, int64_t V,
+                              int64_t stride, float *row_loss, float *row_lse, float *loss_out,
+                              int32_t *good_out, hipStream_t stream) {
+  using namespace uly;
+  int rc = check_logits(logits, n, V, stride);
+  if (rc) return rc;
+  if (!labels || !row_loss || !row_lse || !loss_out || !good_out) return ULY_E_NULL;
+  const size_t lb = span_bytes(n, stride, V), rb = (size_t)n * 4;
+  if (overlaps(row_loss, rb, row_lse, rb) || overlaps(row_loss, rb, logits, lb) ||
+      overlaps(row_lse, rb, logits, lb) || overlaps(row_loss, rb, labels, rb) || overlaps(row_lse, rb, labels, rb))
+    return ULY_E_ALIAS;
+  return launch_ce_fwd(logits, stride, labels, n, V, row_loss, row_lse, loss_out, good_out, stream);
+}
+
+extern "C" int sp_loss_aggregate(int32_t n_ranks, const float *const *rank_loss,
+                                 const int32_t *const *rank_good, float *total_out,
+                                 float *row_grad_scale_out, hipStream_t stream) {
+  using namespace uly;
+  if (!rank_loss || !rank_good || !total_out || !row_grad_scale_out) return ULY_E_NULL;
+  if (n_ranks < 1 || n_ranks > kMaxParts) return ULY_E_SHAPE;
+  for (int r = 0; r < n_ranks; ++r)
+    if (!rank_loss[r] || !rank_good[r]) return ULY_E_NULL;
+  if (total_out == row_grad_scale_out) return ULY_E_ALIAS;
+  return launch_loss_aggregate(n_ranks, rank_loss, rank_good, total_out, row_grad_scale_out, stream);
+}
+
+extern "C" int shifted_ce_bwd(const uint16_t *logits, const int32_t *labels, const float *row_lse,
+                              const float *row_grad_scale, int64_t n, int64_t V, int64_t stride,
+                              uint16_t *dlogits, int64_t dstride, hipStream_t stream) {
+  using namespace uly;
+  int rc = check_logits(logits, n, V, stride);
+  if (rc) return rc;
+  if ((rc = check_logits(dlogits, n, V, dstride))) return rc;
+  if (!labels || !row_lse || !row_grad_scale) return ULY_E_NULL;
+  const bool in_place = (const void *)dlogits == (const void *)logits && dstride == stride;
+  if (!in_place && overlaps(dlogits, span_bytes(n, dstride, V), logits, span_bytes(n, stride, V)))
+    return ULY_E_ALIAS;
+  return launch_ce_bwd(logits, stride, labels, row_lse, row_grad_scale, n, V, dlogits, dstride, stream);
+}

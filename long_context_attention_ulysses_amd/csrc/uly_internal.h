@@ -89,4 +89,18 @@ int launch_lse_merge(int n_parts, const bf16_t *const *o, const float *const *ls
 int launch_grad_sum(int n_parts, const bf16_t *const *parts, bf16_t *out, int64_t rows, int width,
                     int64_t part_stride, int64_t out_stride, hipStream_t stream);
 
+// Shifted-label cross-entropy of one rank: per-row loss and log-sum-exp,
+// then the rank's mean loss over good rows and its good count.
+int launch_ce_fwd(const bf16_t *logits, int64_t stride, const int32_t *labels, int64_t n, int64_t V,
+                  float *row_loss, float *row_lse, float *loss_out, int32_t *good_out, hipStream_t stream);
+
+// Weighted aggregation over ranks and the per-row gradient scale.
+int launch_loss_aggregate(int n_ranks, const float *const *loss, const int32_t *const *good, float *total,
+                          float *row_scale, hipStream_t stream);
+
+// Gradient of the aggregate loss with respect to one rank's logits.
+int launch_ce_bwd(const bf16_t *logits, int64_t stride, const int32_t *labels, const float *row_lse,
+                  const float *row_scale, int64_t n, int64_t V, bf16_t *grad, int64_t gstride,
+                  hipStream_t stream);
+
 }  // namespace uly

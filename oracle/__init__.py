@@ -13,6 +13,9 @@ carries the citations):
   attn_bwd                    its textbook gradient
   lse_merge                   ring attention: softmax over the union of
                               disjoint key blocks from per-block results
+  shift_labels / shifted_ce / sp_loss_aggregate / shifted_ce_grad
+                              the per-rank loss from pre-shifted labels and
+                              its weighted aggregation over the SP ranks
 """
 from __future__ import annotations
 
@@ -202,3 +205,68 @@ def lse_merge(o_parts: Sequence[np.ndarray], lse_parts: Sequence[np.ndarray]
         w = np.where(empty, 0.0, np.exp(l - np.where(empty, 0.0, lse)))  # [h, N]
         o += w.T[:, :, None] * oj
     return o, lse
+
+
+# ------------------------------------------------------------------ O5 ----
+# "Deepspeed Ulysses/ALST integration", opening post, step 2: each rank
+# computes the loss of its token shard from shift_labels (-100 = no loss);
+# the ranks' losses are combined as sum_r loss_r * good_r / max(sum_r good_r,
+# 1), good_r = the rank's count of labels != -100. "Ulysses sequence
+# parallelism", Configure: labels are shifted before sharding.
+
+IGNORE = -100
+
+
+def shift_labels(labels: np.ndarray) -> np.ndarray:
+    """Pre-shifted labels of a whole sequence: position i is trained to
+    predict token i+1, so its label is labels[i+1]; the last position has
+    none (-100)."""
+    lab = np.asarray(labels, dtype=np.int64)
+    out = np.full(lab.shape, IGNORE, dtype=np.int64)
+    out[:-1] = lab[1:]
+    return out
+
+
+def shifted_ce(logits: np.ndarray, labels: np.ndarray) -> Tuple[np.ndarray, np.ndarray, float, int]:
+    """One rank: logits [n, V] (bf16 bits or floats), labels [n].
+    Returns (row_loss [n], row_lse [n], rank mean loss, good count), fp64.
+    Row loss = log sum_v exp(logit_v) - logit_y for labels in [0, V), 0 for
+    the others; the rank's loss is the mean over good rows (0 if none)."""
+    x = _as_f64(logits)
+    lab = np.asarray(labels, dtype=np.int64)
+    n, V = x.shape
+    row_lse = np.empty(n)
+    row_loss = np.zeros(n)
+    good = 0
+    for r in range(n):
+        m = np.max(x[r])
+        row_lse[r] = m + np.log(np.sum(np.exp(x[r] - m)))
+        if 0 <= lab[r] < V:
+            row_loss[r] = row_lse[r] - x[r, lab[r]]
+            good += 1
+    loss = float(np.sum(row_loss) / good) if good else 0.0
+    return row_loss, row_lse, loss, good
+
+
+def sp_loss_aggregate(rank_losses: Sequence[float], rank_goods: Sequence[int]) -> float:
+    """sum_r loss_r * good_r / max(sum_r good_r, 1)."""
+    total = 0.0
+    for l, g in zip(rank_losses, rank_goods):
+        total += float(l) * int(g)
+    return total / max(int(sum(int(g) for g in rank_goods)), 1)
+
+
+def shifted_ce_grad(logits: np.ndarray, labels: np.ndarray, total_good: int) -> np.ndarray:
+    """Gradient of the aggregate with respect to one rank's logits:
+    (softmax(row) - onehot(y)) / max(G, 1) for good rows, 0 otherwise."""
+    x = _as_f64(logits)
+    lab = np.asarray(labels, dtype=np.int64)
+    n, V = x.shape
+    g = np.zeros_like(x)
+    for r in range(n):
+        if 0 <= lab[r] < V:
+            p = np.exp(x[r] - np.max(x[r]))
+            p /= np.sum(p)
+            p[lab[r]] -= 1.0
+            g[r] = p / max(int(total_good), 1)
+    return g
