@@ -184,6 +184,65 @@ def ring_step(uly, torch, w, x_seq, dy_seq, reps=3):
     }
 
 
+def loss_step(uly, torch, w, reps=3):
+    """The shifted-label loss of one rank's n tokens at the Qwen3-4B vocabulary:
+    the rank's cross-entropy (reads the logits once), the aggregation over the
+    P ranks' scalars, and the gradient (reads the logits once, writes the
+    gradient once). Medians over `reps`."""
+    import numpy as np
+
+    import workloads
+    n, V, P = w.n, workloads.VOCAB, w.P
+    logits = workloads.gen_logits_device(n, V, seed=w.seed + 77).view(n, V)
+    labels = torch.from_numpy(workloads.gen_shift_labels(n, V, seed=w.seed + 78)).cuda()
+    grad = torch.empty_like(logits)
+    row_loss = torch.empty((n,), dtype=torch.float32, device="cuda")
+    row_lse = torch.empty((n,), dtype=torch.float32, device="cuda")
+    loss = torch.empty((P,), dtype=torch.float32, device="cuda")
+    good = torch.empty((P,), dtype=torch.int32, device="cuda")
+    total = torch.empty((1,), dtype=torch.float32, device="cuda")
+    scale = torch.empty((1,), dtype=torch.float32, device="cuda")
+
+    def fwd():
+        uly.shifted_ce_fwd(logits, labels, row_loss, row_lse, loss[0:1], good[0:1])
+
+    def agg():  # the other ranks' scalars stand in as copies of this one's
+        loss[1:].fill_(0.0)
+        uly.sp_loss_aggregate([loss[r:r + 1] for r in range(P)], [good[r:r + 1] for r in range(P)], total, scale)
+
+    def bwd():
+        uly.shifted_ce_bwd(logits, labels, row_lse, scale, grad)
+
+    def timed(fn):
+        fn()
+        ts = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    good[1:].fill_(0)
+    t_fwd = timed(fwd)
+    agg()
+    t_bwd = timed(bwd)
+    nbytes = n * V * 2
+    out = {
+        "tokens": n, "vocab": V,
+        "fwd_ms": round(t_fwd, 4), "fwd_gbps": round(nbytes / (t_fwd * 1e-3) / 1e9, 1),
+        "fwd_frac_hbm": round(nbytes / (t_fwd * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "bwd_ms": round(t_bwd, 4), "bwd_gbps": round(2 * nbytes / (t_bwd * 1e-3) / 1e9, 1),
+        "bwd_frac_hbm": round(2 * nbytes / (t_bwd * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "rank_loss": round(float(loss[0].item()), 5),
+    }
+    del logits, grad
+    return out
+
+
 def csrc_digest():
     """sha256 over the HIP sources (names and bytes), to tell whether stored
     counter readings still describe the kernels being run."""
@@ -286,6 +345,7 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=9216,
                     help="tokens of the oracle's CPU-baseline sample (0 = skip)")
     ap.add_argument("--no-ring", action="store_true", help="skip the ring-attention measurement")
+    ap.add_argument("--no-loss", action="store_true", help="skip the shifted-label loss measurement")
     ap.add_argument("--traffic-summary", metavar="PMC_DIR",
                     help="write profiles/traffic_<workload>.txt from two rocprofv3 counter runs and exit")
     args = ap.parse_args()
@@ -444,6 +504,9 @@ def main():
     if not args.no_ring and cu is None:
         log("ring attention step (rank %d of %d) ..." % (P - 1, P))
         result["ring"] = ring_step(uly, torch, w, x_seq, dy_seq)
+    if not args.no_loss:
+        log("shifted-label loss (%d tokens x %d vocab) ..." % (w.n, 151936))
+        result["loss"] = loss_step(uly, torch, w)
     if args.cpu_tokens > 0:
         log("cpu baseline: oracle on %d tokens ..." % args.cpu_tokens)
         result["cpu_baseline"] = cpu_baseline(w, min(args.cpu_tokens, w.N))

@@ -207,3 +207,29 @@ def normal_bf16(shape, seed: int, sigma: float = 1.0) -> np.ndarray:
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 99])))
     vals = rng.standard_normal(int(np.prod(shape)), dtype=np.float32) * np.float32(sigma)
     return f32_to_bf16_bits(vals).reshape(shape)
+
+
+# Vocabulary of the Qwen3-4B-shaped workloads (the model the pages benchmark).
+VOCAB = 151936
+
+
+def gen_logits_device(n: int, V: int, seed: int, sigma: float = 2.0):
+    """Synthetic logits [n, V] as bf16 bit patterns (int16) drawn directly on
+    the GPU with torch's seeded generator (a few GB do not round-trip through
+    the host), N(0, sigma^2) rounded to bf16."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    x = torch.randn((n, V), generator=g, device="cuda", dtype=torch.bfloat16)
+    x.mul_(sigma)
+    return x.view(torch.int16)
+
+
+def gen_shift_labels(n: int, V: int, seed: int, ignore_frac: float = 0.1) -> np.ndarray:
+    """Pre-shifted labels of one rank's n tokens: uniform token ids in
+    [0, V), with a leading prompt-like run of -100 (no loss) covering
+    ignore_frac of the tokens."""
+    rng = np.random.default_rng(seed)
+    lab = rng.integers(0, V, size=n).astype(np.int32)
+    lab[: int(n * ignore_frac)] = -100
+    return lab
