@@ -311,9 +311,9 @@ def write_traffic_summary(workload: str, pmc_dir: str):
         "workload": "%s head shard, one bench step (--steps 1 --warmup 0)" % workload,
         "commands": [
             "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $PMC -o fetch "
-            "-- python3 $REPO/bench.py --workload %s --steps 1 --warmup 0 --cpu-tokens 0" % workload,
+            "-- python3 $REPO/bench.py --workload %s --steps 1 --warmup 0 --cpu-tokens 0 --no-ring --no-loss" % workload,
             "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $PMC -o write "
-            "-- python3 $REPO/bench.py --workload %s --steps 1 --warmup 0 --cpu-tokens 0" % workload,
+            "-- python3 $REPO/bench.py --workload %s --steps 1 --warmup 0 --cpu-tokens 0 --no-ring --no-loss" % workload,
             "python3 $REPO/bench.py --workload %s --traffic-summary $PMC" % workload,
         ],
         "calibration": {
