@@ -19,7 +19,8 @@
  *  - Tensors are bfloat16 bit patterns (uint16_t), LSE and D are float32.
  *  - All tensor pointers are device pointers; the caller allocates and owns
  *    all memory. The library allocates nothing and keeps no mutable global
- *    state apart from a per-thread error message.
+ *    state apart from a per-thread error message (and, once TiledMLP has run
+ *    on a device, that device's hipBLASLt handle).
  *  - Tensor pointers must be 16-byte aligned and token strides must be
  *    multiples of 8 elements (16 bytes); otherwise ULY_E_ALIGN.
  *  - Strides are in elements. Within a token row, heads are d elements apart.
@@ -308,6 +309,40 @@ int sp_loss_aggregate(int32_t n_ranks, const float *const *rank_loss,
 int shifted_ce_bwd(const uint16_t *logits, const int32_t *labels, const float *row_lse,
                    const float *row_grad_scale, int64_t n, int64_t V, int64_t stride,
                    uint16_t *dlogits, int64_t dstride, hipStream_t stream);
+
+/*
+ * TiledMLP: the model's SwiGLU MLP run over the sequence in token tiles, the
+ * second memory component of ALST next to Ulysses ("Ulysses sequence
+ * parallelism", intro note on ALST; "Ulysses Sequence Parallelism for
+ * Million-Token Context Training", Additional Kernels; the pages give only
+ * the name). Per token:
+ *   gu = x W_gu^T (gate | up, 2I values),  a = silu(gate) * up,  y = a W_down^T.
+ * Only one tile's gu and a exist at a time (in ws); the backward pass
+ * recomputes them tile by tile. The GEMMs (bf16 inputs, float32
+ * accumulation) run in hipBLASLt; the SwiGLU steps are HIP kernels.
+ *
+ * x, y, dy, dx [n][H] bf16, contiguous; w_gu [2I][H] (gate rows, then up
+ * rows; nn.Linear's [out][in]); w_down [H][I]; dw_gu [2I][H] and dw_down
+ * [H][I] float32. H and I multiples of 8; all pointers 16-byte aligned.
+ * tile: tokens per tile (>= 1; the last tile may be shorter).
+ * ws: at least tiled_mlp_workspace_bytes(tile, H, I) bytes, 256-byte aligned
+ * (two [tile][2I] and two [tile][I] bf16 buffers plus 64 MiB for hipBLASLt).
+ * tiled_mlp_bwd writes dx and, with accumulate == 0, overwrites dw_gu and
+ * dw_down (accumulate != 0 adds to them).
+ * On first use on a device the library creates one hipBLASLt handle for it
+ * and keeps it until the process ends.
+ * Errors: ULY_E_NULL, ULY_E_SHAPE, ULY_E_ALIGN, ULY_E_WORKSPACE, ULY_E_ALIAS
+ * (an output overlaps an input, another output or ws), ULY_E_HIP (a launch or
+ * hipBLASLt call failed; see uly_last_error()).
+ */
+size_t tiled_mlp_workspace_bytes(int64_t tile, int32_t H, int32_t I);
+int tiled_mlp_fwd(const uint16_t *x, const uint16_t *w_gu, const uint16_t *w_down, uint16_t *y,
+                  int64_t n, int32_t H, int32_t I, int64_t tile, void *ws, size_t ws_bytes,
+                  hipStream_t stream);
+int tiled_mlp_bwd(const uint16_t *x, const uint16_t *w_gu, const uint16_t *w_down,
+                  const uint16_t *dy, uint16_t *dx, float *dw_gu, float *dw_down, int64_t n,
+                  int32_t H, int32_t I, int64_t tile, int32_t accumulate, void *ws,
+                  size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

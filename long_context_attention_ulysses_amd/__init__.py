@@ -6,7 +6,8 @@ hand-written HIP for gfx950; this package is its thin Python binding. The
 same attention calls plus a merge of per-block results and a sum of
 per-block gradients also serve ring attention, the variant the pages
 contrast with Ulysses; the shifted-label loss and its weighted aggregation
-over the SP ranks close the step.
+over the SP ranks close the step; TiledMLP runs the model's MLP over token
+tiles.
 """
 from ._lib import (  # noqa: F401
     EXPORTED,
@@ -27,6 +28,9 @@ from ._lib import (  # noqa: F401
     shifted_ce_fwd,
     sp_loss_aggregate,
     status_string,
+    tiled_mlp_bwd,
+    tiled_mlp_fwd,
+    tiled_mlp_workspace_bytes,
     ulysses_check_cu_seqlens,
     ulysses_head_to_seq,
     ulysses_seq_to_head,

@@ -65,6 +65,9 @@ _SIGS = {
     "shifted_ce_fwd": ([_p, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p], ctypes.c_int),
     "sp_loss_aggregate": ([_i32, ctypes.POINTER(_p), ctypes.POINTER(_p), _p, _p, _p], ctypes.c_int),
     "shifted_ce_bwd": ([_p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _p], ctypes.c_int),
+    "tiled_mlp_workspace_bytes": ([_i64, _i32, _i32], _sz),
+    "tiled_mlp_fwd": ([_p, _p, _p, _p, _i64, _i32, _i32, _i64, _p, _sz, _p], ctypes.c_int),
+    "tiled_mlp_bwd": ([_p, _p, _p, _p, _p, _p, _p, _i64, _i32, _i32, _i64, _i32, _p, _sz, _p], ctypes.c_int),
 }
 for _name, (_args, _res) in _SIGS.items():
     _f = getattr(_L, _name)
@@ -287,3 +290,41 @@ def shifted_ce_bwd(logits, labels, row_lse, row_grad_scale, dlogits, stream=None
     _check(_L.shifted_ce_bwd(_ptr(logits), _ptr(labels), _ptr(row_lse), _ptr(row_grad_scale), n, V,
                              _row_stride(logits, V), _ptr(dlogits), _row_stride(dlogits, V), _stream(stream)),
            "shifted_ce_bwd")
+
+
+def tiled_mlp_workspace_bytes(tile: int, H: int, I: int) -> int:
+    return int(_L.tiled_mlp_workspace_bytes(tile, H, I))
+
+
+def _contig(t, shape):
+    if tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor of shape %s" % (tuple(shape),))
+
+
+def tiled_mlp_fwd(x, w_gu, w_down, y, tile: int, ws=None, stream=None) -> None:
+    """y [n, H] = SwiGLU MLP of x [n, H] with w_gu [2I, H], w_down [H, I]
+    (bf16 bits), over token tiles of `tile`."""
+    n, H = x.shape
+    I = w_down.shape[1]
+    for t, s in ((x, (n, H)), (w_gu, (2 * I, H)), (w_down, (H, I)), (y, (n, H))):
+        _contig(t, s)
+    if ws is None:
+        ws = _workspace(tiled_mlp_workspace_bytes(tile, H, I), x)
+    _check(_L.tiled_mlp_fwd(_ptr(x), _ptr(w_gu), _ptr(w_down), _ptr(y), n, H, I, tile, _ptr(ws),
+                            ws.numel() * ws.element_size(), _stream(stream)), "tiled_mlp_fwd")
+
+
+def tiled_mlp_bwd(x, w_gu, w_down, dy, dx, dw_gu, dw_down, tile: int, accumulate: bool = False, ws=None,
+                  stream=None) -> None:
+    """dx [n, H] (bf16) and the float32 weight gradients dw_gu [2I, H],
+    dw_down [H, I] of the SwiGLU MLP, recomputing each tile's activations."""
+    n, H = x.shape
+    I = w_down.shape[1]
+    for t, s in ((x, (n, H)), (w_gu, (2 * I, H)), (w_down, (H, I)), (dy, (n, H)), (dx, (n, H)),
+                 (dw_gu, (2 * I, H)), (dw_down, (H, I))):
+        _contig(t, s)
+    if ws is None:
+        ws = _workspace(tiled_mlp_workspace_bytes(tile, H, I), x)
+    _check(_L.tiled_mlp_bwd(_ptr(x), _ptr(w_gu), _ptr(w_down), _ptr(dy), _ptr(dx), _ptr(dw_gu), _ptr(dw_down), n,
+                            H, I, tile, int(bool(accumulate)), _ptr(ws), ws.numel() * ws.element_size(),
+                            _stream(stream)), "tiled_mlp_bwd")

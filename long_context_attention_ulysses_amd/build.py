@@ -22,6 +22,10 @@ HIPCC_FLAGS = [
     "-Wall",
 ]
 
+# The TiledMLP GEMMs go to hipBLASLt. In a process that has imported torch,
+# the already-loaded copy with the same soname is the one used.
+LINK_FLAGS = ["-L/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib", "-lhipblaslt"]
+
 
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
@@ -31,7 +35,7 @@ def build(verbose: bool = False, extra=None) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc] + HIPCC_FLAGS + list(extra or []) + ["-I", os.path.join(ROOT, "include"), "-I", CSRC,
-                                                          "-o", tmp] + sources()
+                                                          "-o", tmp] + sources() + LINK_FLAGS
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

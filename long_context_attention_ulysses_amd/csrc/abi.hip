@@ -16,6 +16,11 @@ int set_hip_error(hipError_t e, const char *where) {
   return ULY_E_HIP;
 }
 
+int set_error_text(const char *msg) {
+  snprintf(g_last_error, sizeof(g_last_error), "%s", msg);
+  return ULY_E_HIP;
+}
+
 namespace {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -454,4 +459,73 @@ extern "C" int shifted_ce_bwd(const uint16_t *logits, const int32_t *labels, con
   if (!in_place && overlaps(dlogits, span_bytes(n, dstride, V), logits, span_bytes(n, stride, V)))
     return ULY_E_ALIAS;
   return launch_ce_bwd(logits, stride, labels, row_lse, row_grad_scale, n, V, dlogits, dstride, stream);
+}
+
+extern "C" size_t tiled_mlp_workspace_bytes(int64_t tile, int32_t H, int32_t I) {
+  if (tile <= 0 || H <= 0 || I <= 0) return 0;
+  return uly::mlp_ws_layout(tile, H, I).total;
+}
+
+namespace uly {
+namespace {
+
+int check_mlp(const void *x, const void *w_gu, const void *w_down, int64_t n, int32_t H, int32_t I,
+              int64_t tile, const void *ws, size_t ws_bytes) {
+  if (!x || !w_gu || !w_down) return ULY_E_NULL;
+  if (n <= 0 || H <= 0 || I <= 0 || tile <= 0) return ULY_E_SHAPE;
+  if (H % 8 || I % 8) return ULY_E_ALIGN;
+  if (n * H >= ((int64_t)1 << 40) || tile * I * 2 >= ((int64_t)1 << 31)) return ULY_E_SHAPE;
+  if (!aligned16(x) || !aligned16(w_gu) || !aligned16(w_down)) return ULY_E_ALIGN;
+  if (!ws || ws_bytes < mlp_ws_layout(tile, H, I).total || (reinterpret_cast<uintptr_t>(ws) & 255u))
+    return ULY_E_WORKSPACE;
+  return ULY_OK;
+}
+
+}  // namespace
+}  // namespace uly
+
+extern "C" int tiled_mlp_fwd(const uint16_t *x, const uint16_t *w_gu, const uint16_t *w_down, uint16_t *y,
+                             int64_t n, int32_t H, int32_t I, int64_t tile, void *ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  using namespace uly;
+  int rc = check_mlp(x, w_gu, w_down, n, H, I, tile, ws, ws_bytes);
+  if (rc) return rc;
+  if (!y) return ULY_E_NULL;
+  if (!aligned16(y)) return ULY_E_ALIGN;
+  const size_t xb = (size_t)n * H * 2, wgb = (size_t)2 * I * H * 2, wdb = (size_t)H * I * 2;
+  const size_t wsb = mlp_ws_layout(tile, H, I).total;
+  if (overlaps(y, xb, x, xb) || overlaps(y, xb, w_gu, wgb) || overlaps(y, xb, w_down, wdb) || overlaps(ws, wsb, y, xb) ||
+      overlaps(ws, wsb, x, xb) || overlaps(ws, wsb, w_gu, wgb) || overlaps(ws, wsb, w_down, wdb))
+    return ULY_E_ALIAS;
+  MlpPtrs p{reinterpret_cast<const bf16_t *>(x), reinterpret_cast<const bf16_t *>(w_gu),
+            reinterpret_cast<const bf16_t *>(w_down), nullptr, reinterpret_cast<bf16_t *>(y), nullptr, nullptr,
+            nullptr, static_cast<char *>(ws)};
+  return launch_mlp(false, p, n, H, I, tile, false, stream);
+}
+
+extern "C" int tiled_mlp_bwd(const uint16_t *x, const uint16_t *w_gu, const uint16_t *w_down, const uint16_t *dy,
+                             uint16_t *dx, float *dw_gu, float *dw_down, int64_t n, int32_t H, int32_t I,
+                             int64_t tile, int32_t accumulate, void *ws, size_t ws_bytes, hipStream_t stream) {
+  using namespace uly;
+  int rc = check_mlp(x, w_gu, w_down, n, H, I, tile, ws, ws_bytes);
+  if (rc) return rc;
+  if (!dy || !dx || !dw_gu || !dw_down) return ULY_E_NULL;
+  if (!aligned16(dy) || !aligned16(dx) || !aligned16(dw_gu) || !aligned16(dw_down)) return ULY_E_ALIGN;
+  const size_t xb = (size_t)n * H * 2, wgb = (size_t)2 * I * H * 2, wdb = (size_t)H * I * 2;
+  const size_t gwg = (size_t)2 * I * H * 4, gwd = (size_t)H * I * 4;
+  const size_t wsb = mlp_ws_layout(tile, H, I).total;
+  const void *ins[4] = {x, w_gu, w_down, dy};
+  const size_t inb[4] = {xb, wgb, wdb, xb};
+  const void *outs[4] = {dx, dw_gu, dw_down, ws};
+  const size_t outb[4] = {xb, gwg, gwd, wsb};
+  for (int o = 0; o < 4; ++o) {
+    for (int i = 0; i < 4; ++i)
+      if (overlaps(outs[o], outb[o], ins[i], inb[i])) return ULY_E_ALIAS;
+    for (int o2 = o + 1; o2 < 4; ++o2)
+      if (overlaps(outs[o], outb[o], outs[o2], outb[o2])) return ULY_E_ALIAS;
+  }
+  MlpPtrs p{reinterpret_cast<const bf16_t *>(x), reinterpret_cast<const bf16_t *>(w_gu),
+            reinterpret_cast<const bf16_t *>(w_down), reinterpret_cast<const bf16_t *>(dy), nullptr,
+            reinterpret_cast<bf16_t *>(dx), dw_gu, dw_down, static_cast<char *>(ws)};
+  return launch_mlp(true, p, n, H, I, tile, accumulate != 0, stream);
 }

@@ -14,6 +14,10 @@ constexpr int kMaxSwapRuns = 32;
 // Records a HIP error message for uly_last_error() and returns ULY_E_HIP.
 int set_hip_error(hipError_t e, const char *where);
 
+// Records a message for uly_last_error() and returns ULY_E_HIP (failures of
+// library calls other than HIP's own).
+int set_error_text(const char *msg);
+
 // Packs (to_head) or unpacks the token-split tensor; arguments validated.
 int launch_swap(bool to_head, const bf16_t *src, bf16_t *dst, int64_t n, int P, int nseg,
                 const int32_t *seg_heads, int d, hipStream_t stream);
@@ -102,5 +106,36 @@ int launch_loss_aggregate(int n_ranks, const float *const *loss, const int32_t *
 int launch_ce_bwd(const bf16_t *logits, int64_t stride, const int32_t *labels, const float *row_lse,
                   const float *row_scale, int64_t n, int64_t V, bf16_t *grad, int64_t gstride,
                   hipStream_t stream);
+
+// TiledMLP workspace regions (byte offsets) for tiles of `tile` tokens:
+// gate|up [tile][2I], activation and its gradient [tile][I], gate|up
+// gradient [tile][2I] (bf16), then the GEMM library's workspace.
+constexpr size_t kMlpBlasWs = (size_t)64 << 20;
+struct MlpWs {
+  size_t gu, act, dact, dgu, blas, total;
+};
+inline MlpWs mlp_ws_layout(int64_t tile, int H, int I) {
+  (void)H;
+  MlpWs w;
+  w.gu = 0;
+  w.act = w.gu + align256((size_t)tile * 2 * I * 2);
+  w.dact = w.act + align256((size_t)tile * I * 2);
+  w.dgu = w.dact + align256((size_t)tile * I * 2);
+  w.blas = w.dgu + align256((size_t)tile * 2 * I * 2);
+  w.total = w.blas + kMlpBlasWs;
+  return w;
+}
+
+struct MlpPtrs {
+  const bf16_t *x, *w_gu, *w_down, *dy;
+  bf16_t *y, *dx;
+  float *dw_gu, *dw_down;
+  char *ws;
+};
+
+// Forward (y) or backward (dx, dw_gu, dw_down; added to when accumulate)
+// of the SwiGLU MLP over token tiles; arguments validated.
+int launch_mlp(bool bwd, const MlpPtrs &p, int64_t n, int H, int I, int64_t tile, bool accumulate,
+               hipStream_t stream);
 
 }  // namespace uly

@@ -16,6 +16,9 @@ carries the citations):
   shift_labels / shifted_ce / sp_loss_aggregate / shifted_ce_grad
                               the per-rank loss from pre-shifted labels and
                               its weighted aggregation over the SP ranks
+  swiglu_mlp / swiglu_mlp_bwd the MLP that TiledMLP runs over token tiles
+                              (here untiled: tiling changes memory, not
+                              the result)
 """
 from __future__ import annotations
 
@@ -270,3 +273,44 @@ def shifted_ce_grad(logits: np.ndarray, labels: np.ndarray, total_good: int) -> 
             p[lab[r]] -= 1.0
             g[r] = p / max(int(total_good), 1)
     return g
+
+
+# ------------------------------------------------------------------ O6 ----
+# TiledMLP ("Ulysses sequence parallelism", intro note on ALST; "Ulysses
+# Sequence Parallelism for Million-Token Context Training", Additional
+# Kernels: named only). The plainest reading: the model's SwiGLU MLP, applied
+# to every token; processing the tokens in tiles only bounds the memory of
+# the intermediates. Weights in nn.Linear layout [out][in]; w_gu stacks the
+# gate rows over the up rows.
+
+def _silu_parts(g: np.ndarray):
+    s = 1.0 / (1.0 + np.exp(-g))
+    return s, g * s
+
+
+def swiglu_mlp(x: np.ndarray, w_gu: np.ndarray, w_down: np.ndarray) -> np.ndarray:
+    """y = (silu(x Wg^T) * (x Wu^T)) Wd^T, fp64. x [n, H], w_gu [2I, H], w_down [H, I]."""
+    xd, wgu, wd = _as_f64(x), _as_f64(w_gu), _as_f64(w_down)
+    I = wd.shape[1]
+    g = xd @ wgu[:I].T
+    u = xd @ wgu[I:].T
+    _, silu = _silu_parts(g)
+    return (silu * u) @ wd.T
+
+
+def swiglu_mlp_bwd(x: np.ndarray, w_gu: np.ndarray, w_down: np.ndarray, dy: np.ndarray):
+    """Gradients of sum(dy * y): (dx [n, H], dw_gu [2I, H], dw_down [H, I]), fp64.
+    With s = sigmoid(g): da = dy Wd; dWd = dy^T a; du = da silu(g);
+    dg = da u s (1 + g (1 - s)); dx = [dg | du] W_gu; dW_gu = [dg | du]^T x."""
+    xd, wgu, wd, dyd = _as_f64(x), _as_f64(w_gu), _as_f64(w_down), _as_f64(dy)
+    I = wd.shape[1]
+    g = xd @ wgu[:I].T
+    u = xd @ wgu[I:].T
+    s, silu = _silu_parts(g)
+    a = silu * u
+    da = dyd @ wd
+    dw_down = dyd.T @ a
+    du = da * silu
+    dg = da * u * s * (1.0 + g * (1.0 - s))
+    dgu = np.concatenate([dg, du], axis=1)
+    return dgu @ wgu, dgu.T @ xd, dw_down
