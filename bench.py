@@ -243,6 +243,55 @@ def loss_step(uly, torch, w, reps=3):
     return out
 
 
+def mlp_step(uly, torch, w, tile=4096, reps=3):
+    """TiledMLP over one rank's n tokens at the Qwen3-4B MLP shape (H = 2560,
+    I = 9728), tiles of `tile` tokens: forward, and backward with the
+    recompute. Counted work: 6nHI flop forward, 12nHI backward (the
+    recompute of the gate/up GEMM, 4nHI more, is executed but not counted).
+    Medians over `reps`."""
+    import numpy as np
+
+    import workloads
+    n, H, I = w.n, workloads.MLP_HIDDEN, workloads.MLP_INTER
+    x = workloads.gen_normal_device((n, H), seed=w.seed + 80)
+    dy = workloads.gen_normal_device((n, H), seed=w.seed + 81)
+    w_gu = workloads.gen_normal_device((2 * I, H), seed=w.seed + 82, sigma=1.0 / np.sqrt(H))
+    w_down = workloads.gen_normal_device((H, I), seed=w.seed + 83, sigma=1.0 / np.sqrt(I))
+    y = torch.empty_like(x)
+    dx = torch.empty_like(x)
+    dw_gu = torch.empty((2 * I, H), dtype=torch.float32, device="cuda")
+    dw_down = torch.empty((H, I), dtype=torch.float32, device="cuda")
+    ws = torch.empty(uly.tiled_mlp_workspace_bytes(tile, H, I), dtype=torch.uint8, device="cuda")
+
+    def timed(fn):
+        fn()
+        ts = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    t_fwd = timed(lambda: uly.tiled_mlp_fwd(x, w_gu, w_down, y, tile, ws))
+    t_bwd = timed(lambda: uly.tiled_mlp_bwd(x, w_gu, w_down, dy, dx, dw_gu, dw_down, tile, False, ws))
+    nhi = float(n) * H * I
+    out = {
+        "tokens": n, "hidden": H, "intermediate": I, "tile": tile,
+        "fwd_ms": round(t_fwd, 3), "fwd_tflops": round(6 * nhi / (t_fwd * 1e-3) / 1e12, 2),
+        "bwd_ms": round(t_bwd, 3), "bwd_tflops": round(12 * nhi / (t_bwd * 1e-3) / 1e12, 2),
+        "bwd_exec_tflops": round(16 * nhi / (t_bwd * 1e-3) / 1e12, 2),
+        "fwd_frac_peak": round(6 * nhi / (t_fwd * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "intermediate_bytes_tiled": int(ws.numel()),
+        "intermediate_bytes_untiled": int(n * 6 * I * 2),
+    }
+    del x, dy, y, dx, dw_gu, dw_down, ws
+    return out
+
+
 def csrc_digest():
     """sha256 over the HIP sources (names and bytes), to tell whether stored
     counter readings still describe the kernels being run."""
@@ -311,9 +360,9 @@ def write_traffic_summary(workload: str, pmc_dir: str):
         "workload": "%s head shard, one bench step (--steps 1 --warmup 0)" % workload,
         "commands": [
             "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $PMC -o fetch "
-            "-- python3 $REPO/bench.py --workload %s --steps 1 --warmup 0 --cpu-tokens 0 --no-ring --no-loss" % workload,
+            "-- python3 $REPO/bench.py --workload %s --steps 1 --warmup 0 --cpu-tokens 0 --no-ring --no-loss --no-mlp" % workload,
             "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $PMC -o write "
-            "-- python3 $REPO/bench.py --workload %s --steps 1 --warmup 0 --cpu-tokens 0 --no-ring --no-loss" % workload,
+            "-- python3 $REPO/bench.py --workload %s --steps 1 --warmup 0 --cpu-tokens 0 --no-ring --no-loss --no-mlp" % workload,
             "python3 $REPO/bench.py --workload %s --traffic-summary $PMC" % workload,
         ],
         "calibration": {
@@ -346,6 +395,7 @@ def main():
                     help="tokens of the oracle's CPU-baseline sample (0 = skip)")
     ap.add_argument("--no-ring", action="store_true", help="skip the ring-attention measurement")
     ap.add_argument("--no-loss", action="store_true", help="skip the shifted-label loss measurement")
+    ap.add_argument("--no-mlp", action="store_true", help="skip the TiledMLP measurement")
     ap.add_argument("--traffic-summary", metavar="PMC_DIR",
                     help="write profiles/traffic_<workload>.txt from two rocprofv3 counter runs and exit")
     args = ap.parse_args()
@@ -507,6 +557,9 @@ def main():
     if not args.no_loss:
         log("shifted-label loss (%d tokens x %d vocab) ..." % (w.n, 151936))
         result["loss"] = loss_step(uly, torch, w)
+    if not args.no_mlp:
+        log("TiledMLP (%d tokens) ..." % w.n)
+        result["mlp"] = mlp_step(uly, torch, w)
     if args.cpu_tokens > 0:
         log("cpu baseline: oracle on %d tokens ..." % args.cpu_tokens)
         result["cpu_baseline"] = cpu_baseline(w, min(args.cpu_tokens, w.N))

@@ -213,16 +213,26 @@ def normal_bf16(shape, seed: int, sigma: float = 1.0) -> np.ndarray:
 VOCAB = 151936
 
 
-def gen_logits_device(n: int, V: int, seed: int, sigma: float = 2.0):
-    """Synthetic logits [n, V] as bf16 bit patterns (int16) drawn directly on
-    the GPU with torch's seeded generator (a few GB do not round-trip through
-    the host), N(0, sigma^2) rounded to bf16."""
+def gen_normal_device(shape, seed: int, sigma: float = 1.0):
+    """N(0, sigma^2) values rounded to bf16, as bit patterns (int16), drawn
+    directly on the GPU with torch's seeded generator (large inputs do not
+    round-trip through the host)."""
     import torch
     g = torch.Generator(device="cuda")
     g.manual_seed(seed)
-    x = torch.randn((n, V), generator=g, device="cuda", dtype=torch.bfloat16)
+    x = torch.randn(tuple(shape), generator=g, device="cuda", dtype=torch.bfloat16)
     x.mul_(sigma)
     return x.view(torch.int16)
+
+
+def gen_logits_device(n: int, V: int, seed: int, sigma: float = 2.0):
+    """Synthetic logits [n, V] (see gen_normal_device)."""
+    return gen_normal_device((n, V), seed, sigma)
+
+
+# MLP shape of the Qwen3-4B-shaped workloads: hidden size and SwiGLU
+# intermediate size.
+MLP_HIDDEN, MLP_INTER = 2560, 9728
 
 
 def gen_shift_labels(n: int, V: int, seed: int, ignore_frac: float = 0.1) -> np.ndarray:
