@@ -76,7 +76,7 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_bwd_dq_kernel(BwdArgs a
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31;
   const int hi32 = lane >> 5;
 
@@ -145,9 +145,9 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_bwd_dq_kernel(BwdArgs a
   // Buffer views: K and V rows of KV head g (rows >= N read as zeros; their
   // scores are masked) and K^T of head g.
   const uint32_t ksb = (uint32_t)(a.k_stride * 2), vsb = (uint32_t)(a.v_stride * 2);
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + (int64_t)g * D, head_rows_bytes(a.N, a.k_stride, D));
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v + (int64_t)g * D, head_rows_bytes(a.N, a.v_stride, D));
-  const __amdgpu_buffer_rsrc_t trs = make_rsrc(a.kt + (int64_t)g * D * a.Np, (uint32_t)(D * a.Np * 2));
+  const bf16_t *kbase = a.k + (int64_t)g * D, *vbase = a.v + (int64_t)g * D;
+  const uint32_t kbytes = head_rows_bytes(a.N, a.k_stride, D), vbytes = head_rows_bytes(a.N, a.v_stride, D);
+  const BufRes trs = make_rsrc(a.kt + (int64_t)g * D * a.Np, (uint32_t)(D * a.Np * 2));
   uint32_t koff[C::NI / C::NW], voff[C::NI / C::NW], toff[C::NI / C::NW];
 #pragma unroll
   for (int i = 0; i < C::NI / C::NW; ++i) {
@@ -160,14 +160,18 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_bwd_dq_kernel(BwdArgs a
     toff[i] = (uint32_t)(d * a.Np * 2) + (((s & 7) ^ ((d >> 1) & 7)) << 4);
   }
 
+  // K and V rows from tile row t0 on (resources from row t0 to the end of
+  // row N-1).
   auto issue = [&](int kt, bf16_t *ks_, bf16_t *vs_, bf16_t *ts_) {
     const uint32_t t0 = (uint32_t)kt * C::BN;
+    const BufRes krs = make_rsrc(kbase + (int64_t)t0 * a.k_stride, kbytes - t0 * ksb);
+    const BufRes vrs = make_rsrc(vbase + (int64_t)t0 * a.v_stride, vbytes - t0 * vsb);
 #pragma unroll
     for (int i = 0; i < C::NI / C::NW; ++i) {
       const int u = w + i * C::NW;
-      dma16(krs, koff[i] + t0 * ksb, 0, lds_ptr(ks_ + u * 512));
-      dma16(vrs, voff[i] + t0 * vsb, 0, lds_ptr(vs_ + u * 512));
-      dma16(trs, toff[i], t0 * 2, lds_ptr(ts_ + u * 512));
+      dma16(krs, koff[i], 0, ks_ + u * 512);
+      dma16(vrs, voff[i], 0, vs_ + u * 512);
+      dma16(trs, toff[i], t0 * 2, ts_ + u * 512);
     }
   };
 
@@ -229,6 +233,7 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_bwd_dq_kernel(BwdArgs a
     compute(t, ks_, vs_, ts_);
   };
 
+  wait_vmcnt<0>();  // Q, dO fragments loaded: only tile copies are counted below
   if (kt0 < kt1) issue(kt0, k0, v0, t0_);
   if (kt0 + 1 < kt1) issue(kt0 + 1, k1, v1, t1_);
   for (int kt = kt0; kt < kt1; kt += 3) {
@@ -370,29 +375,31 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
   auto issue_rows = [&](int t, bf16_t *qs, bf16_t *ds, bf16_t *dts, float *ls) {
     const int h = tile_head(t);
     const uint32_t u0 = tile_u0(t);
-    // Q and dO rows of head h (rows >= N read as zeros; they are masked).
-    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.q + (int64_t)h * D, head_rows_bytes(a.N, a.q_stride, D));
-    const __amdgpu_buffer_rsrc_t drs =
-        make_rsrc(a.dout + (int64_t)h * D, head_rows_bytes(a.N, a.do_stride, D));
-    const __amdgpu_buffer_rsrc_t dtr = make_rsrc(a.dot + (int64_t)h * D * a.Np, (uint32_t)(D * a.Np * 2));
+    // Q and dO rows of head h from row u0 to the end of row N-1 (rows >= N
+    // read as zeros; they are masked).
+    const BufRes qrs = make_rsrc(a.q + (int64_t)u0 * a.q_stride + (int64_t)h * D,
+                                 head_rows_bytes(a.N, a.q_stride, D) - u0 * qsb);
+    const BufRes drs = make_rsrc(a.dout + (int64_t)u0 * a.do_stride + (int64_t)h * D,
+                                 head_rows_bytes(a.N, a.do_stride, D) - u0 * dsb);
+    const BufRes dtr = make_rsrc(a.dot + (int64_t)h * D * a.Np, (uint32_t)(D * a.Np * 2));
 #pragma unroll
     for (int i = 0; i < C::NI / C::NW; ++i) {
       const int u = w + i * C::NW;
-      dma16(qrs, qoff[i] + u0 * qsb, 0, lds_ptr(qs + u * 512));
-      dma16(drs, doff[i] + u0 * dsb, 0, lds_ptr(ds + u * 512));
-      dma16(dtr, toff[i], u0 * 2, lds_ptr(dts + u * 512));
+      dma16(qrs, qoff[i], 0, qs + u * 512);
+      dma16(drs, doff[i], 0, ds + u * 512);
+      dma16(dtr, toff[i], u0 * 2, dts + u * 512);
     }
     if (w < 2) {  // wave 0: LSE*log2e of the 64 rows, wave 1: D; rows >= N read as zeros
       const float *src = (w == 0 ? a.lse2 : a.delta) + (int64_t)h * a.Np;
-      dma4(make_rsrc(src, (uint32_t)(a.N * 4)), (u0 + lane) * 4, 0, lds_ptr(ls + w * C::BQ));
+      dma4(make_rsrc(src + u0, (uint32_t)((a.N - u0) * 4)), lane * 4, 0, ls + w * C::BQ);
     }
   };
   auto issue_qt = [&](int t, bf16_t *qts) {
     const int h = tile_head(t);
     const uint32_t u0 = tile_u0(t);
-    const __amdgpu_buffer_rsrc_t qtr = make_rsrc(a.qt + (int64_t)h * D * a.Np, (uint32_t)(D * a.Np * 2));
+    const BufRes qtr = make_rsrc(a.qt + (int64_t)h * D * a.Np, (uint32_t)(D * a.Np * 2));
 #pragma unroll
-    for (int i = 0; i < C::NI / C::NW; ++i) dma16(qtr, toff[i], u0 * 2, lds_ptr(qts + (w + i * C::NW) * 512));
+    for (int i = 0; i < C::NI / C::NW; ++i) dma16(qtr, toff[i], u0 * 2, qts + (w + i * C::NW) * 512);
   };
   auto active = [&](int t) {
     const int64_t u0 = tile_u0(t);
@@ -524,6 +531,7 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
       }
     };
 
+    wait_vmcnt<0>();  // K or V fragments loaded: only tile copies are counted below
     if (ntiles > 0) {
       issue_rows(0, q0s, d0s, dt0, ls0);
       issue_qt(0, qt0);

@@ -76,24 +76,57 @@ __device__ __forceinline__ int rt_off(int r, int c) {
 // a trans tile.
 __device__ __forceinline__ int tr_off(int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 7)) << 3); }
 
-// Buffer resource over the `bytes` bytes at `base`: buffer loads at byte
-// offsets >= bytes return zeros (raw buffer, stride 0).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+// Buffer resource (four SGPRs) over the `bytes` bytes at `base`: buffer
+// loads at byte offsets >= bytes return zeros (raw buffer, stride 0).
+typedef uint32_t BufRes __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ BufRes make_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  BufRes r;
+  r[0] = (uint32_t)b;
+  r[1] = (uint32_t)(b >> 32) & 0xFFFFu;
+  r[2] = bytes;
+  r[3] = 0x00020000u;
+  return r;
+}
+
+// LDS byte address of a (generic) pointer into a __shared__ array, made
+// wave-uniform: the low 32 bits of a flat address in the LDS aperture (taking
+// them needs no null check, unlike a cast to the LDS address space).
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(p));
 }
 
 // Wave-wide direct-to-LDS copy of 16 bytes per lane from buffer `r` at byte
 // offset voff + soff (voff per lane, soff wave-uniform): lane i's bytes land
-// at lds + 16 i. `lds` must be wave-uniform. Range checking uses voff only.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
-                                      ULY_LDS void *lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, soff, 0, 0);
+// at lds + 16 i (`lds` points into a __shared__ array, wave-uniform).
+// Range checking uses voff only.
+//
+// Written as inline asm so that the compiler keeps no record of the copy:
+// it cannot tell which LDS bytes an in-flight copy writes and would
+// otherwise wait for every copy still in flight before each LDS read, which
+// drains the prefetch ring. The caller orders the copy against its readers
+// with wait_vmcnt and barrier (both also compiler memory fences), and keeps
+// voff in a loop-invariant register (move the tile's start into the resource
+// base instead), so that no copy waits for a register it reads. The leading
+// s_nop 4 gives the five wait states a VMEM instruction needs after a VALU
+// write of an SGPR it reads (a resource word restored by v_readlane) and
+// covers the one after the M0 write: the compiler's hazard check does not
+// look into inline asm.
+__device__ __forceinline__ void dma16(BufRes r, uint32_t voff, uint32_t soff, const void *lds) {
+  const uint32_t m0 = lds_addr(lds);
+  __asm__ volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                   :
+                   : "v"(voff), "s"(r), "s"(soff), "{m0}"(m0)
+                   : "memory");
 }
 
 // Same with 4 bytes per lane (lane i -> lds + 4 i).
-__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
-                                     ULY_LDS void *lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 4, voff, soff, 0, 0);
+__device__ __forceinline__ void dma4(BufRes r, uint32_t voff, uint32_t soff, const void *lds) {
+  const uint32_t m0 = lds_addr(lds);
+  __asm__ volatile("s_nop 4\n\tbuffer_load_dword %0, %1, %2 offen lds"
+                   :
+                   : "v"(voff), "s"(r), "s"(soff), "{m0}"(m0)
+                   : "memory");
 }
 
 // Bytes from the start of a head's first row to the end of its row N-1 in a
@@ -103,22 +136,26 @@ __host__ __device__ __forceinline__ uint32_t head_rows_bytes(int64_t N, int64_t 
   return (uint32_t)(((N - 1) * stride + d) * 2);
 }
 
-template <typename T>
-__device__ __forceinline__ ULY_LDS void *lds_ptr(T *p) {
-  return (ULY_LDS void *)p;
-}
 
 // Wait until at most N vector-memory operations of this wave are in flight
-// (s_waitcnt vmcnt(N); the other counters are left unconstrained).
+// (s_waitcnt vmcnt(N); the other counters are left unconstrained). The empty
+// asm statements keep the compiler from moving memory accesses across.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
+  __asm__ volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+  __asm__ volatile("" ::: "memory");
 }
 
 // Workgroup barrier without a memory fence: LDS tiles written by
 // direct-to-LDS copies are covered by the explicit vmcnt waits before it.
-__device__ __forceinline__ void barrier() { __builtin_amdgcn_s_barrier(); }
+// The empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
 
 // Workgroup barrier after this wave's own LDS stores (s_waitcnt lgkmcnt(0),
 // then s_barrier), without waiting for direct-to-LDS copies still in flight.

@@ -74,7 +74,7 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_fwd_kernel(FwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31;
   const int hi32 = lane >> 5;
 
@@ -130,8 +130,9 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_fwd_kernel(FwdArgs a) {
   // Buffer views: K rows of KV head g (rows >= N read as zeros, and their
   // scores are masked) and V^T of head g.
   const uint32_t kstride_b = (uint32_t)(a.k_stride * 2);
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + (int64_t)g * D, head_rows_bytes(a.N, a.k_stride, D));
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.vt + (int64_t)g * D * a.Np, (uint32_t)(D * a.Np * 2));
+  const bf16_t *kbase = a.k + (int64_t)g * D;
+  const uint32_t kbytes = head_rows_bytes(a.N, a.k_stride, D);
+  const BufRes vrs = make_rsrc(a.vt + (int64_t)g * D * a.Np, (uint32_t)(D * a.Np * 2));
   // Per-lane byte offsets of this wave's 16-byte slots inside a tile.
   uint32_t koff[C::NI / C::NW], voff[C::NI / C::NW];
 #pragma unroll
@@ -144,14 +145,17 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_fwd_kernel(FwdArgs a) {
   }
 
   // Direct-to-LDS copies of tile kt: this wave's share of the 1 KiB blocks.
+  // K rows from tile row t0 on: the resource starts at row t0 and still ends
+  // after row N-1.
   auto issue = [&](int kt, bf16_t *ks_, bf16_t *vs_) {
     const uint32_t t0 = (uint32_t)kt * C::BN;
+    const BufRes krs = make_rsrc(kbase + (int64_t)t0 * a.k_stride, kbytes - t0 * kstride_b);
 #pragma unroll
     for (int i = 0; i < C::NI / C::NW; ++i)
-      dma16(krs, koff[i] + t0 * kstride_b, 0, lds_ptr(ks_ + (w + i * C::NW) * 512));
+      dma16(krs, koff[i], 0, ks_ + (w + i * C::NW) * 512);
 #pragma unroll
     for (int i = 0; i < C::NI / C::NW; ++i)
-      dma16(vrs, voff[i], t0 * 2, lds_ptr(vs_ + (w + i * C::NW) * 512));
+      dma16(vrs, voff[i], t0 * 2, vs_ + (w + i * C::NW) * 512);
   };
 
   auto compute = [&](int kt, const bf16_t *ks_, const bf16_t *vs_) {
@@ -245,6 +249,7 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_fwd_kernel(FwdArgs a) {
     compute(t, ks_, vs_);
   };
 
+  wait_vmcnt<0>();  // Q fragments loaded: only tile copies are counted below
   if (kt0 < kt1) issue(kt0, k0, v0);
   if (kt0 + 1 < kt1) issue(kt0 + 1, k1, v1);
   for (int kt = kt0; kt < kt1; kt += 3) {
