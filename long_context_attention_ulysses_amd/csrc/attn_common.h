@@ -96,6 +96,18 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(p));
 }
 
+// The resource words as SGPR values: the asm operands below must be SGPRs,
+// and the compiler does not move a value it takes for divergent into them by
+// itself (free where the value is already uniform).
+__device__ __forceinline__ BufRes uniform(BufRes r) {
+  BufRes u;
+  u[0] = __builtin_amdgcn_readfirstlane(r[0]);
+  u[1] = __builtin_amdgcn_readfirstlane(r[1]);
+  u[2] = __builtin_amdgcn_readfirstlane(r[2]);
+  u[3] = __builtin_amdgcn_readfirstlane(r[3]);
+  return u;
+}
+
 // Wave-wide direct-to-LDS copy of 16 bytes per lane from buffer `r` at byte
 // offset voff + soff (voff per lane, soff wave-uniform): lane i's bytes land
 // at lds + 16 i (`lds` points into a __shared__ array, wave-uniform).
@@ -114,6 +126,8 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // look into inline asm.
 __device__ __forceinline__ void dma16(BufRes r, uint32_t voff, uint32_t soff, const void *lds) {
   const uint32_t m0 = lds_addr(lds);
+  r = uniform(r);
+  soff = __builtin_amdgcn_readfirstlane(soff);
   __asm__ volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                    :
                    : "v"(voff), "s"(r), "s"(soff), "{m0}"(m0)
@@ -123,6 +137,8 @@ __device__ __forceinline__ void dma16(BufRes r, uint32_t voff, uint32_t soff, co
 // Same with 4 bytes per lane (lane i -> lds + 4 i).
 __device__ __forceinline__ void dma4(BufRes r, uint32_t voff, uint32_t soff, const void *lds) {
   const uint32_t m0 = lds_addr(lds);
+  r = uniform(r);
+  soff = __builtin_amdgcn_readfirstlane(soff);
   __asm__ volatile("s_nop 4\n\tbuffer_load_dword %0, %1, %2 offen lds"
                    :
                    : "v"(voff), "s"(r), "s"(soff), "{m0}"(m0)
