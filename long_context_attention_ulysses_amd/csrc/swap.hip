@@ -81,10 +81,14 @@ __global__ void __launch_bounds__(kSwapThreads) swap_kernel(SwapArgs a) {
 
 // Token-major kernel: a block copies kRowTokens whole token rows. For every
 // vector j of a token's chunk-ordered row (chunk p, local vector k) it looks
-// up the matching vector of the token-split row in a per-block LDS table, so
-// both sides are walked in long contiguous stretches. Loads and stores are
-// nontemporal: every byte is touched once. 512 threads x 4 vectors in flight
-// and 4 tokens per block measured best for a 12-KiB row.
+// up, in two per-block LDS tables, the matching vector of the token-split row
+// and the vector's place in the chunk tensor, so both sides are walked in long
+// contiguous stretches and the copy loop does no integer division (one
+// multiply-shift for the token). Loads and stores are nontemporal: every byte
+// is touched once. 512 threads x 4 vectors in flight and 4 tokens per block
+// measured best for 8- and 12-KiB rows (8 or 16 tokens per block, or 8
+// vectors in flight, were 2-10 % slower). Indexes are 32-bit: the boundary
+// rejects tensors of 2^31 vectors or more.
 constexpr int kRowThreads = 512;
 constexpr int kRowTokens = 4;
 constexpr int kRowInFlight = 4;
@@ -99,11 +103,16 @@ struct RowArgs {
   int nseg;
   uint32_t seg_base_vec[8];   // segment start (vectors) in the token-split row
   uint32_t seg_local_vec[8];  // vectors of one rank's block of the segment
+  FastDiv row_div;            // division by row_vec
 };
 
 template <bool kToHead>
 __global__ void __launch_bounds__(kRowThreads) swap_rows_kernel(RowArgs a) {
-  __shared__ uint32_t tab[kMaxRowVec];  // chunk-ordered index -> token-split index
+  // Vector j of a token's chunk-ordered row (chunk p, vector k of the chunk
+  // row): stab[j] = its vector in the token-split row; ctab[j] = its offset
+  // in the chunk tensor for token 0 (p * n * chunk_vec + k).
+  __shared__ uint32_t stab[kMaxRowVec];
+  __shared__ uint32_t ctab[kMaxRowVec];
   for (uint32_t j = threadIdx.x; j < a.row_vec; j += kRowThreads) {
     const uint32_t p = j / a.chunk_vec, k = j - p * a.chunk_vec;
     uint32_t kk = k, src = 0;
@@ -115,39 +124,42 @@ __global__ void __launch_bounds__(kRowThreads) swap_rows_kernel(RowArgs a) {
       }
       kk -= L;
     }
-    tab[j] = src;
+    stab[j] = src;
+    ctab[j] = p * a.n * a.chunk_vec + k;
   }
   __syncthreads();
   const uint32_t t0 = blockIdx.x * kRowTokens;
   const uint32_t nt = (a.n - t0) < (uint32_t)kRowTokens ? (a.n - t0) : (uint32_t)kRowTokens;
   const uint32_t total = nt * a.row_vec;
+  const u32x4 *src = a.src;
+  u32x4 *dst = a.dst;
   constexpr int U = kRowInFlight;
   for (uint32_t base = threadIdx.x; base < total; base += kRowThreads * U) {
     u32x4 v[U];
-    int64_t di[U];
+    uint32_t di[U];
+    bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t i = base + u * kRowThreads;
-      di[u] = -1;
-      if (i < total) {
-        const uint32_t tl = i / a.row_vec;  // token within the block
+      ok[u] = i < total;
+      if (ok[u]) {
+        const uint32_t tl = a.row_div.q(i);  // token within the block
         const uint32_t j = i - tl * a.row_vec;
         const uint32_t t = t0 + tl;
-        const uint32_t p = j / a.chunk_vec;
-        const int64_t c_idx = ((int64_t)p * a.n + t) * a.chunk_vec + (j - p * a.chunk_vec);
-        const int64_t s_idx = (int64_t)t * a.row_vec + tab[j];
+        const uint32_t c_idx = t * a.chunk_vec + ctab[j];
+        const uint32_t s_idx = t * a.row_vec + stab[j];
         if (kToHead) {
-          v[u] = __builtin_nontemporal_load(a.src + s_idx);
+          v[u] = __builtin_nontemporal_load(src + s_idx);
           di[u] = c_idx;
         } else {
-          v[u] = __builtin_nontemporal_load(a.src + c_idx);
+          v[u] = __builtin_nontemporal_load(src + c_idx);
           di[u] = s_idx;
         }
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (di[u] >= 0) __builtin_nontemporal_store(v[u], a.dst + di[u]);
+      if (ok[u]) __builtin_nontemporal_store(v[u], dst + di[u]);
   }
 }
 
@@ -163,6 +175,7 @@ static int launch_swap_rows(bool to_head, const bf16_t *src, bf16_t *dst, int64_
   for (int s = 0; s < nseg; ++s) H += seg_heads[s];
   a.row_vec = (uint32_t)(H * d / 8);
   a.chunk_vec = (uint32_t)(H / P * d / 8);
+  a.row_div = FastDiv(a.row_vec);
   a.nseg = nseg;
   uint32_t base = 0;
   for (int s = 0; s < 8; ++s) {
