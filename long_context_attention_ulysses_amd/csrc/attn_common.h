@@ -48,7 +48,7 @@ __device__ __forceinline__ bf16x8 cvt8(float a0, float a1, float a2, float a3, f
 
 // ---- LDS tiles -------------------------------------------------------------
 // Two tile shapes, both 64 rows/positions deep and filled by direct-to-LDS
-// copies (global_load_lds_dwordx4: lane i's 16 bytes land at base + 16 i, so
+// copies (buffer_load_dwordx4 ... lds: lane i's 16 bytes land at base + 16 i, so
 // any permutation of 16-byte chunks inside a 1 KiB block is free to build):
 //
 //   row tile   [64 rows][D]: a token's d values in one row; the 16-byte
