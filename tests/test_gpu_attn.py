@@ -168,8 +168,8 @@ def _sample_rows(N, n_local, count, seed):
 @pytest.mark.parametrize("name", ["8k", "64k", "varlen", "256k"])
 def test_workload_head_shard_sampled(name):
     """Rank 0's head shard at the workload's full size, in the launch shape the
-    benchmark times; oracle on sampled query rows (O, LSE, dQ) and on the
-    last 128 keys (dK, dV)."""
+    benchmark times; oracle on sampled query rows (O, LSE, dQ), on the last
+    128 keys (dK, dV) and, where the oracle is fast enough, on the first 128."""
     w = workloads.WORKLOADS[name]
     print("workload %s N=%d hq=%d hkv=%d" % (name, w.N, w.hq, w.hkv), flush=True)
     qkv = workloads.gen_head_shard(w, 0)
@@ -190,6 +190,14 @@ def test_workload_head_shard_sampled(name):
     assert_close(name + " dQ[rows]", oracle.bf16_to_f64(dq[rows]), dq_ref, GRAD_MAX_ABS, GRAD_REL)
     assert_close(name + " dK[tail]", oracle.bf16_to_f64(dk[klo:]), dk_ref, GRAD_MAX_ABS, GRAD_REL)
     assert_close(name + " dV[tail]", oracle.bf16_to_f64(dv[klo:]), dv_ref, GRAD_MAX_ABS, GRAD_REL)
+    if name in ("8k", "varlen"):
+        # The first key block sees every query tile of its document(s), the
+        # longest walk through the dK/dV kernel's rings (the oracle needs a
+        # few seconds for it at these sizes).
+        _, dk_ref, dv_ref = oracle.attn_bwd(q, k, v, dy, w.scale, True, cu, rows=rows[:1], key_lo=0,
+                                            key_hi=128, want_dq=False)
+        assert_close(name + " dK[head]", oracle.bf16_to_f64(dk[:128]), dk_ref, GRAD_MAX_ABS, GRAD_REL)
+        assert_close(name + " dV[head]", oracle.bf16_to_f64(dv[:128]), dv_ref, GRAD_MAX_ABS, GRAD_REL)
     for t, nm in ((o, "O"), (dq, "dQ"), (dk, "dK"), (dv, "dV")):
         assert np.all(np.isfinite(oracle.bf16_to_f64(t))), nm + " has unwritten/non-finite elements"
 
