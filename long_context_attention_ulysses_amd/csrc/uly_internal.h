@@ -37,9 +37,11 @@ inline size_t fwd_ws_bytes(int64_t N, int hkv, int d) {
 }
 
 // Backward workspace regions (byte offsets): D and LSE*log2(e) as float
-// [hq][pad64(N)], then K^T, Q^T, dO^T as contraction-ordered bf16 copies.
+// [hq][pad64(N)], then K^T, Q^T, dO^T as contraction-ordered bf16 copies,
+// then the int32 order of the dK/dV kernel's key blocks for packed
+// documents (pad64(N) / 64 entries).
 struct BwdWs {
-  size_t delta, lse2, kt, qt, dot, total;
+  size_t delta, lse2, kt, qt, dot, korder, total;
 };
 
 inline BwdWs bwd_ws_layout(int64_t N, int hq, int hkv, int d) {
@@ -50,7 +52,8 @@ inline BwdWs bwd_ws_layout(int64_t N, int hq, int hkv, int d) {
   w.kt = w.lse2 + align256((size_t)hq * np * 4);
   w.qt = w.kt + align256((size_t)hkv * d * np * 2);
   w.dot = w.qt + align256((size_t)hq * d * np * 2);
-  w.total = w.dot + align256((size_t)hq * d * np * 2);
+  w.korder = w.dot + align256((size_t)hq * d * np * 2);
+  w.total = w.korder + align256(np / 64 * 4);
   return w;
 }
 
