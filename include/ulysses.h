@@ -164,7 +164,10 @@ int attn_fwd_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v, uin
  * LSE*log2(e), [hq][roundup(N, 64)] each, then transposed copies of K, Q and
  * dO (hkv, hq and hq heads of d * roundup(N, 64) bf16), then an int32 array
  * of roundup(N, 64) / 64 entries (the varlen workgroup order of the dK/dV
- * pass), each region rounded up to 256 bytes. */
+ * pass), and, when there are fewer than 256 (128-key block, KV head) pairs,
+ * float32 partial dK/dV of s * N * hkv * 2 * d values, s = min(4,
+ * ceil(256 / pairs)) (the dK/dV pass then splits each pair's queries over s
+ * workgroups); each region rounded up to 256 bytes. */
 size_t attn_bwd_workspace_bytes(int64_t N, int32_t hq, int32_t hkv, int32_t d, int32_t n_seqs);
 
 /*

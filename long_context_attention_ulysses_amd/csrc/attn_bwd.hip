@@ -49,6 +49,8 @@ struct BwdArgs {
   const int32_t *cu;
   int n_seqs;
   const int32_t *korder;  // packed documents: key blocks by decreasing work
+  int ksplit;             // dK/dV: workgroups per (key block, KV head)
+  float *dkv_part;        // dK/dV partials [ksplit][N][hkv][2][d] when ksplit > 1
 };
 
 // ------------------------------------------------------------ dq kernel ----
@@ -282,7 +284,7 @@ struct DkvCfg {
 // dV product uses. Each wave then holds one of K or V and one of the dK or
 // dV accumulators, so a wave fits in 256 registers and two waves share each
 // SIMD: one's MFMAs run while the other computes exponentials or dS.
-template <int D>
+template <int D, bool kSplit>
 __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs a) {
   using C = DkvCfg<D>;
   __shared__ __align__(16) bf16_t q0s[C::TILE], q1s[C::TILE];    // Q row tiles
@@ -302,9 +304,12 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
 
   // Heaviest key blocks (earliest keys under the causal mask) first;
   // consecutive ids alternate KV heads.
+  // With a split the pieces of one key block are consecutive ids.
   const int item = blockIdx.x;
   const int g = item % a.hkv;
-  const int kb = a.korder ? a.korder[item / a.hkv] : item / a.hkv;
+  const int kbi = kSplit ? item / a.hkv / a.ksplit : item / a.hkv;
+  const int split = kSplit ? item / a.hkv % a.ksplit : 0;
+  const int kb = a.korder ? a.korder[kbi] : kbi;
   const int64_t k0 = (int64_t)kb * C::BNK;
   const int64_t k_last = (k0 + C::BNK < a.N ? k0 + C::BNK : a.N) - 1;
   const int64_t kw0 = k0 + (int64_t)kbw * 32;
@@ -348,6 +353,9 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
   const int qt1_ = (int)((qr_hi + C::BQ - 1) / C::BQ);
   const int ntq = qt1_ - qt0_;
   const int ntiles = ntq * a.G;  // (head of the group, query tile) pairs
+  // This workgroup's share of them: tiles [tb, te).
+  const int tb = kSplit ? (int)((int64_t)ntiles * split / a.ksplit) : 0;
+  const int te = kSplit ? (int)((int64_t)ntiles * (split + 1) / a.ksplit) : ntiles;
 
   // Per-lane byte offsets of this wave's 16-byte slots inside a tile: row
   // tiles of Q and dO (token stride), trans tiles of Q^T and dO^T.
@@ -439,7 +447,7 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
                     bf16_t *qts_n) __attribute__((always_inline)) {
       wait_vmcnt<C::NI / C::NW>();
       barrier();
-      if (t + 1 < ntiles) issue_rows(t + 1, qs_n, ds_n, dts_n, ls_n);
+      if (t + 1 < te) issue_rows(t + 1, qs_n, ds_n, dts_n, ls_n);
       const int64_t u0 = tile_u0(t);
       const bool act = active(t);
       f32x16 x[2];
@@ -492,7 +500,7 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
         }
       }
       lds_barrier();
-      if (t + 1 < ntiles) issue_qt(t + 1, qts_n);
+      if (t + 1 < te) issue_qt(t + 1, qts_n);
       if constexpr (S) {
         if (act) {
 #pragma unroll
@@ -533,20 +541,20 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
     };
 
     wait_vmcnt<0>();  // K or V fragments loaded: only tile copies are counted below
-    if (ntiles > 0) {
-      issue_rows(0, q0s, d0s, dt0, ls0);
-      issue_qt(0, qt0);
+    if (tb < te) {
+      issue_rows(tb, q0s, d0s, dt0, ls0);
+      issue_qt(tb, qt0);
     }
-    for (int t = 0; t < ntiles; t += 2) {
+    for (int t = tb; t < te; t += 2) {
       tile(t, q0s, d0s, dt0, ls0, qt1, q1s, d1s, dt1, ls1, qt1);
-      if (t + 1 < ntiles) tile(t + 1, q1s, d1s, dt1, ls1, qt0, q0s, d0s, dt0, ls0, qt0);
+      if (t + 1 < te) tile(t + 1, q1s, d1s, dt1, ls1, qt0, q0s, d0s, dt0, ls0, qt0);
     }
     // The last tile's dK update: its Q^T copy is complete once every wave
     // has waited for its own part of it.
     wait_vmcnt<0>();
     barrier();
     if constexpr (!S) {
-      if (pend) dk_update((ntiles - 1) % 2 == 0 ? qt0 : qt1);
+      if (pend) dk_update((te - 1 - tb) % 2 == 0 ? qt0 : qt1);
     }
   };
   if (srole)
@@ -555,19 +563,71 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
     run(std::false_type{});
 
   if (key_ok) {
-    bf16_t *out = srole ? a.dv + key * a.dv_stride + (int64_t)g * D : a.dk + key * a.dk_stride + (int64_t)g * D;
     const float f = srole ? 1.f : a.scale;
+    if constexpr (!kSplit) {
+      bf16_t *out = srole ? a.dv + key * a.dv_stride + (int64_t)g * D : a.dk + key * a.dk_stride + (int64_t)g * D;
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+      for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int d0 = db * 32 + gq * 8 + hi32 * 4;
-        u32x2 pk;
-        pk[0] = pack_bf16x2(acc[db][gq * 4 + 0] * f, acc[db][gq * 4 + 1] * f);
-        pk[1] = pack_bf16x2(acc[db][gq * 4 + 2] * f, acc[db][gq * 4 + 3] * f);
-        *reinterpret_cast<u32x2 *>(out + d0) = pk;
-      }
+        for (int gq = 0; gq < 4; ++gq) {
+          const int d0 = db * 32 + gq * 8 + hi32 * 4;
+          u32x2 pk;
+          pk[0] = pack_bf16x2(acc[db][gq * 4 + 0] * f, acc[db][gq * 4 + 1] * f);
+          pk[1] = pack_bf16x2(acc[db][gq * 4 + 2] * f, acc[db][gq * 4 + 3] * f);
+          *reinterpret_cast<u32x2 *>(out + d0) = pk;
+        }
+    } else {
+      float *out = a.dkv_part + (((int64_t)split * a.N + key) * a.hkv + g) * 2 * D + (srole ? D : 0);
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int d0 = db * 32 + gq * 8 + hi32 * 4;
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[db][gq * 4 + e] * f;
+          *reinterpret_cast<f32x4 *>(out + d0) = v;
+        }
+    }
   }
+}
+
+// Sum of the dK/dV kernel's float32 partials over its query-range split, in
+// split order (deterministic), rounded to bf16 into dk and dv: one thread per
+// 8 values.
+struct PartSumArgs {
+  const float *part;  // [ks][N][hkv][2][d]
+  bf16_t *dk, *dv;
+  int64_t N, dk_stride, dv_stride;
+  int hkv, d, ks;
+  uint32_t total;     // N * hkv * 2 * d / 8
+};
+
+__global__ void __launch_bounds__(256) dkdv_part_sum_kernel(PartSumArgs a) {
+  const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+  if (i >= a.total) return;
+  const uint32_t cpr = (uint32_t)a.d / 8;       // chunks of 8 per (key, head, which) row
+  const uint32_t row = i / cpr, c = i - row * cpr;
+  const int which = (int)(row % 2);             // 0: dK, 1: dV
+  const int64_t kg = row / 2;                   // key * hkv + g
+  const int64_t key = kg / a.hkv;
+  const int g = (int)(kg - key * a.hkv);
+  const size_t split_stride = (size_t)a.N * a.hkv * 2 * a.d;
+  const float *p = a.part + (size_t)row * a.d + c * 8;
+  f32x4 s0 = *reinterpret_cast<const f32x4 *>(p), s1 = *reinterpret_cast<const f32x4 *>(p + 4);
+  for (int s = 1; s < a.ks; ++s) {
+    const f32x4 t0 = *reinterpret_cast<const f32x4 *>(p + s * split_stride);
+    const f32x4 t1 = *reinterpret_cast<const f32x4 *>(p + s * split_stride + 4);
+    s0 += t0;
+    s1 += t1;
+  }
+  u32x4 o;
+  o[0] = pack_bf16x2(s0[0], s0[1]);
+  o[1] = pack_bf16x2(s0[2], s0[3]);
+  o[2] = pack_bf16x2(s1[0], s1[1]);
+  o[3] = pack_bf16x2(s1[2], s1[3]);
+  bf16_t *dst = which ? a.dv + key * a.dv_stride : a.dk + key * a.dk_stride;
+  *reinterpret_cast<u32x4 *>(dst + (int64_t)g * a.d + c * 8) = o;
 }
 
 // Key-block schedule of the dK/dV kernel over packed documents (one
@@ -648,15 +708,36 @@ template <int D>
 int launch_dkdv_cfg(BwdArgs a, hipStream_t stream) {
   using C = DkvCfg<D>;
   a.nblk = (int)((a.N + C::BNK - 1) / C::BNK);
+  a.ksplit = dkdv_ksplit(a.N, a.hkv);
   if (a.korder) {
     const int rc = launch_key_block_order(a.cu, a.n_seqs, a.N, a.causal, C::BNK, a.nblk,
                                           const_cast<int32_t *>(a.korder), stream);
     if (rc) return rc;
   }
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), dim3((unsigned)((int64_t)a.nblk * a.hkv)),
-                     dim3(C::NT), 0, stream, a);
+  if (a.ksplit > 1)
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true>), dim3((unsigned)((int64_t)a.nblk * a.hkv * a.ksplit)),
+                       dim3(C::NT), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false>), dim3((unsigned)((int64_t)a.nblk * a.hkv)), dim3(C::NT),
+                       0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_hip_error(e, "attn_bwd_dkdv_kernel");
+  if (a.ksplit > 1) {
+    PartSumArgs ps;
+    ps.part = a.dkv_part;
+    ps.dk = a.dk;
+    ps.dv = a.dv;
+    ps.N = a.N;
+    ps.dk_stride = a.dk_stride;
+    ps.dv_stride = a.dv_stride;
+    ps.hkv = a.hkv;
+    ps.d = D;
+    ps.ks = a.ksplit;
+    ps.total = (uint32_t)(a.N * a.hkv * 2 * D / 8);
+    hipLaunchKernelGGL(dkdv_part_sum_kernel, dim3((ps.total + 255) / 256), dim3(256), 0, stream, ps);
+    e = hipGetLastError();
+    if (e != hipSuccess) return set_hip_error(e, "dkdv_part_sum_kernel");
+  }
   return 0;
 }
 
@@ -699,6 +780,8 @@ int launch_attn_bwd(const AttnShape &s, const AttnBwdPtrs &p, int parts, hipStre
   a.cu = s.cu;
   a.n_seqs = s.n_seqs;
   a.korder = s.cu ? reinterpret_cast<const int32_t *>(p.ws + L.korder) : nullptr;
+  a.ksplit = 1;
+  a.dkv_part = reinterpret_cast<float *>(p.ws + L.part);
   const int hpw = (a.G % 4 == 0) ? 4 : (a.G % 2 == 0) ? 2 : 1;
   int rc = 0;
   if (parts & 1) {

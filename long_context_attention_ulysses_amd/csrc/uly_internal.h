@@ -36,12 +36,24 @@ inline size_t fwd_ws_bytes(int64_t N, int hkv, int d) {
   return align256((size_t)hkv * d * pad64(N) * sizeof(bf16_t));
 }
 
+// Number of workgroups the dK/dV kernel splits each (128-key block, KV head)
+// pair's query range over: 1 when there are at least 256 pairs (one per CU
+// of the MI355X), else enough to reach 256, at most 4. With a split the
+// kernel writes float32 partial dK/dV and a second pass sums them.
+inline int dkdv_ksplit(int64_t N, int hkv) {
+  const int64_t pairs = (N + 127) / 128 * hkv;
+  if (pairs >= 256) return 1;
+  const int64_t s = (256 + pairs - 1) / pairs;
+  return s < 4 ? (int)s : 4;
+}
+
 // Backward workspace regions (byte offsets): D and LSE*log2(e) as float
 // [hq][pad64(N)], then K^T, Q^T, dO^T as contraction-ordered bf16 copies,
 // then the int32 order of the dK/dV kernel's key blocks for packed
-// documents (pad64(N) / 64 entries).
+// documents (pad64(N) / 64 entries), then, when the dK/dV kernel splits its
+// query ranges, the float32 partials [ksplit][N][hkv][dK, dV][d].
 struct BwdWs {
-  size_t delta, lse2, kt, qt, dot, korder, total;
+  size_t delta, lse2, kt, qt, dot, korder, part, total;
 };
 
 inline BwdWs bwd_ws_layout(int64_t N, int hq, int hkv, int d) {
@@ -53,7 +65,9 @@ inline BwdWs bwd_ws_layout(int64_t N, int hq, int hkv, int d) {
   w.qt = w.kt + align256((size_t)hkv * d * np * 2);
   w.dot = w.qt + align256((size_t)hq * d * np * 2);
   w.korder = w.dot + align256((size_t)hq * d * np * 2);
-  w.total = w.korder + align256(np / 64 * 4);
+  w.part = w.korder + align256(np / 64 * 4);
+  const int ks = dkdv_ksplit(N, hkv);
+  w.total = w.part + (ks > 1 ? align256((size_t)ks * N * hkv * 2 * d * 4) : 0);
   return w;
 }
 

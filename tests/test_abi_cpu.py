@@ -136,5 +136,10 @@ def test_workspaces_grow_linearly_with_n():
         for N in (4096, 65536, 262144):
             f1, f2 = L.attn_fwd_workspace_bytes(N, hq, hkv, d), L.attn_fwd_workspace_bytes(2 * N, hq, hkv, d)
             b1, b2 = L.attn_bwd_workspace_bytes(N, hq, hkv, d, 1), L.attn_bwd_workspace_bytes(2 * N, hq, hkv, d, 1)
-            assert f2 == 2 * f1 and abs(b2 - 2 * b1) <= 2048
-            assert b1 <= N * (2 * hq * 4 + (hkv + 2 * hq) * d * 2) + N // 64 * 4 + 2048
+            assert f2 == 2 * f1
+            # below 256 (128-key block, KV head) pairs the dK/dV pass splits its
+            # query ranges over up to 4 workgroups and keeps float32 partials
+            split_max = 4 * N * hkv * 2 * d * 4 if N // 128 * hkv < 256 else 0
+            assert b1 <= N * (2 * hq * 4 + (hkv + 2 * hq) * d * 2) + N // 64 * 4 + split_max + 2048
+            if N // 128 * hkv >= 256:
+                assert abs(b2 - 2 * b1) <= 2048
