@@ -167,7 +167,10 @@ int attn_fwd_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v, uin
  * pass), and, when there are fewer than 256 (128-key block, KV head) pairs,
  * float32 partial dK/dV of s * N * hkv * 2 * d values, s = min(4,
  * ceil(256 / pairs)) (the dK/dV pass then splits each pair's queries over s
- * workgroups); each region rounded up to 256 bytes. */
+ * workgroups), and, when there are fewer than 512 (query block of 256 / hpw
+ * rows, group of hpw query heads) pairs, hpw the largest of 4, 2, 1 dividing
+ * hq / hkv, float32 partial dQ of s' * N * hq * d values, s' = min(4,
+ * ceil(512 / pairs)); each region rounded up to 256 bytes. */
 size_t attn_bwd_workspace_bytes(int64_t N, int32_t hq, int32_t hkv, int32_t d, int32_t n_seqs);
 
 /*

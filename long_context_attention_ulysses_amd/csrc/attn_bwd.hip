@@ -51,6 +51,8 @@ struct BwdArgs {
   const int32_t *korder;  // packed documents: key blocks by decreasing work
   int ksplit;             // dK/dV: workgroups per (key block, KV head)
   float *dkv_part;        // dK/dV partials [ksplit][N][hkv][2][d] when ksplit > 1
+  int qsplit;             // dq: workgroups per (query block, head group)
+  float *dq_part;         // dQ partials [qsplit][N][hq][d] when qsplit > 1
 };
 
 // ------------------------------------------------------------ dq kernel ----
@@ -70,7 +72,7 @@ struct DqCfg {
   static constexpr int NLW = 3 * NI / NW;  // copies per wave per tile (K, V, K^T)
 };
 
-template <int D, int HPW, int RB>
+template <int D, int HPW, int RB, bool kSplit>
 __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_bwd_dq_kernel(BwdArgs a) {
   using C = DqCfg<D, HPW, RB>;
   __shared__ __align__(16) bf16_t k0[C::TILE], k1[C::TILE], k2[C::TILE];
@@ -83,9 +85,11 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_bwd_dq_kernel(BwdArgs a
   const int l32 = lane & 31;
   const int hi32 = lane >> 5;
 
+  // With a split the pieces of one query block are consecutive ids.
   const int item = blockIdx.x;
   const int hg = item % a.nhg;
-  const int qb = a.nblk - 1 - item / a.nhg;
+  const int qb = a.nblk - 1 - (kSplit ? item / a.nhg / a.qsplit : item / a.nhg);
+  const int split = kSplit ? item / a.nhg % a.qsplit : 0;
   const int64_t q0 = (int64_t)qb * C::BM;
   const int h = hg * HPW + w / RB;
   const int g = (hg * HPW) / a.G;
@@ -132,7 +136,7 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_bwd_dq_kernel(BwdArgs a
   }
   const float delta = dpart + xor32(dpart);
   const float lse2 = row_ok ? a.lse[(int64_t)h * a.N + row] * kLog2e : 0.f;
-  if (row_ok && hi32 == 0) {
+  if (row_ok && hi32 == 0 && split == 0) {
     a.delta[(int64_t)h * a.Np + row] = delta;
     a.lse2[(int64_t)h * a.Np + row] = lse2;
   }
@@ -143,8 +147,11 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_bwd_dq_kernel(BwdArgs a
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
-  const int kt0 = (int)(kv_lo / C::BN);
-  const int kt1 = (int)((kv_hi + C::BN - 1) / C::BN);
+  // Key tiles of the block, and this workgroup's share of them [kt0, kt1).
+  const int kta = (int)(kv_lo / C::BN);
+  const int ktb = (int)((kv_hi + C::BN - 1) / C::BN);
+  const int kt0 = kSplit ? kta + (int)((int64_t)(ktb - kta) * split / a.qsplit) : kta;
+  const int kt1 = kSplit ? kta + (int)((int64_t)(ktb - kta) * (split + 1) / a.qsplit) : ktb;
   // Buffer views: K and V rows of KV head g (rows >= N read as zeros; their
   // scores are masked) and K^T of head g.
   const uint32_t ksb = (uint32_t)(a.k_stride * 2), vsb = (uint32_t)(a.v_stride * 2);
@@ -246,18 +253,64 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_bwd_dq_kernel(BwdArgs a
   }
 
   if (row_ok) {
-    bf16_t *out = a.dq + row * a.dq_stride + (int64_t)h * D;
+    if constexpr (!kSplit) {
+      bf16_t *out = a.dq + row * a.dq_stride + (int64_t)h * D;
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+      for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int d0 = db * 32 + gq * 8 + hi32 * 4;
-        u32x2 pk;
-        pk[0] = pack_bf16x2(acc[db][gq * 4 + 0] * a.scale, acc[db][gq * 4 + 1] * a.scale);
-        pk[1] = pack_bf16x2(acc[db][gq * 4 + 2] * a.scale, acc[db][gq * 4 + 3] * a.scale);
-        *reinterpret_cast<u32x2 *>(out + d0) = pk;
-      }
+        for (int gq = 0; gq < 4; ++gq) {
+          const int d0 = db * 32 + gq * 8 + hi32 * 4;
+          u32x2 pk;
+          pk[0] = pack_bf16x2(acc[db][gq * 4 + 0] * a.scale, acc[db][gq * 4 + 1] * a.scale);
+          pk[1] = pack_bf16x2(acc[db][gq * 4 + 2] * a.scale, acc[db][gq * 4 + 3] * a.scale);
+          *reinterpret_cast<u32x2 *>(out + d0) = pk;
+        }
+    } else {
+      float *out = a.dq_part + (((int64_t)split * a.N + row) * a.hq + h) * D;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int d0 = db * 32 + gq * 8 + hi32 * 4;
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[db][gq * 4 + e] * a.scale;
+          *reinterpret_cast<f32x4 *>(out + d0) = v;
+        }
+    }
   }
+}
+
+// Sum of the dq kernel's float32 partials over its key-range split, in split
+// order (deterministic), rounded to bf16 into dq: one thread per 8 values.
+struct DqSumArgs {
+  const float *part;  // [ks][N][hq][d]
+  bf16_t *dq;
+  int64_t N, dq_stride;
+  int hq, d, ks;
+  uint32_t total;     // N * hq * d / 8
+};
+
+__global__ void __launch_bounds__(256) dq_part_sum_kernel(DqSumArgs a) {
+  const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+  if (i >= a.total) return;
+  const uint32_t cpr = (uint32_t)a.d / 8;  // chunks of 8 per (row, head)
+  const uint32_t rh = i / cpr, c = i - rh * cpr;
+  const int64_t row = rh / a.hq;
+  const int h = (int)(rh - row * a.hq);
+  const size_t split_stride = (size_t)a.N * a.hq * a.d;
+  const float *p = a.part + (size_t)rh * a.d + c * 8;
+  f32x4 s0 = *reinterpret_cast<const f32x4 *>(p), s1 = *reinterpret_cast<const f32x4 *>(p + 4);
+  for (int s = 1; s < a.ks; ++s) {
+    s0 += *reinterpret_cast<const f32x4 *>(p + s * split_stride);
+    s1 += *reinterpret_cast<const f32x4 *>(p + s * split_stride + 4);
+  }
+  u32x4 o;
+  o[0] = pack_bf16x2(s0[0], s0[1]);
+  o[1] = pack_bf16x2(s0[2], s0[3]);
+  o[2] = pack_bf16x2(s1[0], s1[1]);
+  o[3] = pack_bf16x2(s1[2], s1[3]);
+  *reinterpret_cast<u32x4 *>(a.dq + row * a.dq_stride + (int64_t)h * a.d + c * 8) = o;
 }
 
 // ---------------------------------------------------------- dkdv kernel ----
@@ -697,10 +750,29 @@ int launch_dq_cfg(BwdArgs a, hipStream_t stream) {
   using C = DqCfg<D, HPW, RB>;
   a.nblk = (int)((a.N + C::BM - 1) / C::BM);
   a.nhg = a.hq / HPW;
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, HPW, RB>), dim3((unsigned)((int64_t)a.nblk * a.nhg)),
-                     dim3(C::NT), 0, stream, a);
+  a.qsplit = dq_ksplit(a.N, a.hq, a.hkv);
+  if (a.qsplit > 1)
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, HPW, RB, true>),
+                       dim3((unsigned)((int64_t)a.nblk * a.nhg * a.qsplit)), dim3(C::NT), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, HPW, RB, false>), dim3((unsigned)((int64_t)a.nblk * a.nhg)),
+                       dim3(C::NT), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_hip_error(e, "attn_bwd_dq_kernel");
+  if (a.qsplit > 1) {
+    DqSumArgs ps;
+    ps.part = a.dq_part;
+    ps.dq = a.dq;
+    ps.N = a.N;
+    ps.dq_stride = a.dq_stride;
+    ps.hq = a.hq;
+    ps.d = D;
+    ps.ks = a.qsplit;
+    ps.total = (uint32_t)(a.N * a.hq * D / 8);
+    hipLaunchKernelGGL(dq_part_sum_kernel, dim3((ps.total + 255) / 256), dim3(256), 0, stream, ps);
+    e = hipGetLastError();
+    if (e != hipSuccess) return set_hip_error(e, "dq_part_sum_kernel");
+  }
   return 0;
 }
 
@@ -782,6 +854,8 @@ int launch_attn_bwd(const AttnShape &s, const AttnBwdPtrs &p, int parts, hipStre
   a.korder = s.cu ? reinterpret_cast<const int32_t *>(p.ws + L.korder) : nullptr;
   a.ksplit = 1;
   a.dkv_part = reinterpret_cast<float *>(p.ws + L.part);
+  a.qsplit = 1;
+  a.dq_part = reinterpret_cast<float *>(p.ws + L.qpart);
   const int hpw = (a.G % 4 == 0) ? 4 : (a.G % 2 == 0) ? 2 : 1;
   int rc = 0;
   if (parts & 1) {

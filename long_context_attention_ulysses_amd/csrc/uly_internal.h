@@ -47,13 +47,30 @@ inline int dkdv_ksplit(int64_t N, int hkv) {
   return s < 4 ? (int)s : 4;
 }
 
+// Number of workgroups the dq kernel splits each (query block, head group)
+// pair's key range over: 1 when there are at least 512 pairs (two per CU),
+// else enough to reach 512, at most 4. The blocks are BM = 256 / hpw query
+// rows for hpw = 4, 2 or 1 heads per workgroup (the largest dividing the
+// GQA group size). With a split the kernel writes float32 partial dQ and a
+// second pass sums them.
+inline int dq_ksplit(int64_t N, int hq, int hkv) {
+  const int G = hq / hkv;
+  const int hpw = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+  const int64_t bm = 256 / hpw;
+  const int64_t pairs = (N + bm - 1) / bm * (hq / hpw);
+  if (pairs >= 512) return 1;
+  const int64_t s = (512 + pairs - 1) / pairs;
+  return s < 4 ? (int)s : 4;
+}
+
 // Backward workspace regions (byte offsets): D and LSE*log2(e) as float
 // [hq][pad64(N)], then K^T, Q^T, dO^T as contraction-ordered bf16 copies,
 // then the int32 order of the dK/dV kernel's key blocks for packed
 // documents (pad64(N) / 64 entries), then, when the dK/dV kernel splits its
-// query ranges, the float32 partials [ksplit][N][hkv][dK, dV][d].
+// query ranges, the float32 partials [ksplit][N][hkv][dK, dV][d], and when
+// the dq kernel splits its key ranges, the float32 partials [s][N][hq][d].
 struct BwdWs {
-  size_t delta, lse2, kt, qt, dot, korder, part, total;
+  size_t delta, lse2, kt, qt, dot, korder, part, qpart, total;
 };
 
 inline BwdWs bwd_ws_layout(int64_t N, int hq, int hkv, int d) {
@@ -67,7 +84,9 @@ inline BwdWs bwd_ws_layout(int64_t N, int hq, int hkv, int d) {
   w.korder = w.dot + align256((size_t)hq * d * np * 2);
   w.part = w.korder + align256(np / 64 * 4);
   const int ks = dkdv_ksplit(N, hkv);
-  w.total = w.part + (ks > 1 ? align256((size_t)ks * N * hkv * 2 * d * 4) : 0);
+  w.qpart = w.part + (ks > 1 ? align256((size_t)ks * N * hkv * 2 * d * 4) : 0);
+  const int qs = dq_ksplit(N, hq, hkv);
+  w.total = w.qpart + (qs > 1 ? align256((size_t)qs * N * hq * d * 4) : 0);
   return w;
 }
 

@@ -138,8 +138,12 @@ def test_workspaces_grow_linearly_with_n():
             b1, b2 = L.attn_bwd_workspace_bytes(N, hq, hkv, d, 1), L.attn_bwd_workspace_bytes(2 * N, hq, hkv, d, 1)
             assert f2 == 2 * f1
             # below 256 (128-key block, KV head) pairs the dK/dV pass splits its
-            # query ranges over up to 4 workgroups and keeps float32 partials
-            split_max = 4 * N * hkv * 2 * d * 4 if N // 128 * hkv < 256 else 0
+            # query ranges, and below 512 (query block, head group) pairs the dq
+            # pass splits its key ranges, over up to 4 workgroups each, keeping
+            # float32 partials
+            dkdv_split = N // 128 * hkv < 256
+            dq_split = N // 64 * (hq // 4) < 512  # 4 heads per dq workgroup here
+            split_max = (4 * N * hkv * 2 * d * 4 if dkdv_split else 0) + (4 * N * hq * d * 4 if dq_split else 0)
             assert b1 <= N * (2 * hq * 4 + (hkv + 2 * hq) * d * 2) + N // 64 * 4 + split_max + 2048
-            if N // 128 * hkv >= 256:
+            if not dkdv_split and not dq_split:
                 assert abs(b2 - 2 * b1) <= 2048
