@@ -144,7 +144,11 @@ int attn_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *
              size_t ws_bytes, hipStream_t stream);
 
 /* Workspace attn_fwd and attn_fwd_varlen need: hkv * d * roundup(N, 64) * 2
- * bytes, rounded up to 256. */
+ * bytes (the transposed V), rounded up to 256, and, when there are fewer than
+ * 512 (query block of 256 / hpw rows, group of hpw query heads) pairs, hpw
+ * the largest of 4, 2, 1 dividing hq / hkv, s * N * hq * (d + 2) * 4 bytes
+ * more, s = min(4, ceil(512 / pairs)), rounded up to 256: float32 partial
+ * softmax states of the s workgroups that then share each pair's keys. */
 size_t attn_fwd_workspace_bytes(int64_t N, int32_t hq, int32_t hkv, int32_t d);
 
 /*

@@ -108,9 +108,9 @@ int attn_fwd_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint1
       overlaps(o, ob, v, span_bytes(N, vs, (int64_t)hkv * d)) ||
       overlaps(lse, (size_t)N * hq * 4, o, ob))
     return ULY_E_ALIAS;
-  if (!ws || ws_bytes < fwd_ws_bytes(N, hkv, d) || (reinterpret_cast<uintptr_t>(ws) & 255u))
+  if (!ws || ws_bytes < fwd_ws_bytes(N, hq, hkv, d) || (reinterpret_cast<uintptr_t>(ws) & 255u))
     return ULY_E_WORKSPACE;
-  const size_t wb = fwd_ws_bytes(N, hkv, d);
+  const size_t wb = fwd_ws_bytes(N, hq, hkv, d);
   if (overlaps(ws, wb, o, ob) || overlaps(ws, wb, lse, (size_t)N * hq * 4) ||
       overlaps(ws, wb, q, span_bytes(N, qs, (int64_t)hq * d)) ||
       overlaps(ws, wb, k, span_bytes(N, ks, (int64_t)hkv * d)) ||
@@ -265,7 +265,7 @@ int ulysses_head_to_seq(const uint16_t *x_recv, uint16_t *x_seq, int64_t n_local
 size_t attn_fwd_workspace_bytes(int64_t N, int32_t hq, int32_t hkv, int32_t d) {
   (void)hq;
   if (N <= 0 || hkv <= 0 || d <= 0) return 0;
-  return fwd_ws_bytes(N, hkv, d);
+  return fwd_ws_bytes(N, hq, hkv, d);
 }
 
 int attn_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *o, float *lse,

@@ -45,6 +45,8 @@ struct FwdArgs {
   int causal;
   const int32_t *cu;
   int n_seqs;
+  int qsplit;                    // workgroups per (query block, head group)
+  float *opart, *mpart, *lpart;  // partials when qsplit > 1: O [s][N][hq][D], max and sum [s][hq][N]
 };
 
 // Headroom (log2 units) the running max may lag the true max by; see the
@@ -66,7 +68,7 @@ struct FwdCfg {
   static constexpr int NLW = 2 * NI / NW;  // copies per wave per tile (K and V^T)
 };
 
-template <int D, int HPW, int RB>
+template <int D, int HPW, int RB, bool kSplit>
 __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_fwd_kernel(FwdArgs a) {
   using C = FwdCfg<D, HPW, RB>;
   __shared__ __align__(16) bf16_t k0[C::TILE], k1[C::TILE], k2[C::TILE];
@@ -78,10 +80,12 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_fwd_kernel(FwdArgs a) {
   const int l32 = lane & 31;
   const int hi32 = lane >> 5;
 
-  // Heaviest query blocks first; consecutive ids alternate head groups.
+  // Heaviest query blocks first; consecutive ids alternate head groups, and
+  // with a split the pieces of one query block are consecutive.
   const int item = blockIdx.x;
   const int hg = item % a.nhg;
-  const int qb = a.nqb - 1 - item / a.nhg;
+  const int qb = a.nqb - 1 - (kSplit ? item / a.nhg / a.qsplit : item / a.nhg);
+  const int split = kSplit ? item / a.nhg % a.qsplit : 0;
   const int64_t q0 = (int64_t)qb * C::BM;
   const int h = hg * HPW + w / RB;
   const int g = (hg * HPW) / a.G;
@@ -125,8 +129,11 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_fwd_kernel(FwdArgs a) {
     for (int i = 0; i < 16; ++i) acc_o[db][i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  const int kt0 = (int)(kv_lo / C::BN);
-  const int kt1 = (int)((kv_hi + C::BN - 1) / C::BN);
+  // Key tiles of the block, and this workgroup's share of them [kt0, kt1).
+  const int kta = (int)(kv_lo / C::BN);
+  const int ktb = (int)((kv_hi + C::BN - 1) / C::BN);
+  const int kt0 = kSplit ? kta + (int)((int64_t)(ktb - kta) * split / a.qsplit) : kta;
+  const int kt1 = kSplit ? kta + (int)((int64_t)(ktb - kta) * (split + 1) / a.qsplit) : ktb;
   // Buffer views: K rows of KV head g (rows >= N read as zeros, and their
   // scores are masked) and V^T of head g.
   const uint32_t kstride_b = (uint32_t)(a.k_stride * 2);
@@ -258,8 +265,30 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_fwd_kernel(FwdArgs a) {
     if (kt + 2 < kt1) step(kt + 2, k2, v2, k1, v1);
   }
 
-  // Epilogue: O = O^T / l, LSE = (m + log2 l) * ln 2.
+  // Epilogue: O = O^T / l, LSE = (m + log2 l) * ln 2; with a split, the
+  // unnormalised O^T, m and l of this share of the keys.
   const float l_tot = l_run + xor32(l_run);
+  if constexpr (kSplit) {
+    if (row_ok) {
+      float *orow = a.opart + (((int64_t)split * a.N + row) * a.hq + h) * D;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int d0 = db * 32 + gq * 8 + hi32 * 4;
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc_o[db][gq * 4 + e];
+          *reinterpret_cast<f32x4 *>(orow + d0) = v;
+        }
+      if (hi32 == 0) {
+        const int64_t ml = ((int64_t)split * a.hq + h) * a.N + row;
+        a.mpart[ml] = m_run;
+        a.lpart[ml] = l_tot;
+      }
+    }
+    return;
+  }
   if (row_ok) {
     const float inv = 1.f / l_tot;
     bf16_t *orow = a.o + row * a.o_stride + (int64_t)h * D;
@@ -277,15 +306,80 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_fwd_kernel(FwdArgs a) {
   }
 }
 
+// Merge of the forward's partial softmax states over its key-range split:
+// with M = max_s m_s and w_s = 2^(m_s - M), O = sum_s w_s O_s / sum_s w_s l_s
+// and LSE = (M + log2 sum_s w_s l_s) ln 2 (m in log2 units), the same result
+// the unsplit kernel forms from one running state. One thread per 8 values.
+struct FwdMergeArgs {
+  const float *opart, *mpart, *lpart;
+  bf16_t *o;
+  float *lse;
+  int64_t N, o_stride;
+  int hq, d, ks;
+  uint32_t total;  // N * hq * d / 8
+};
+
+__global__ void __launch_bounds__(256) fwd_merge_kernel(FwdMergeArgs a) {
+  const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+  if (i >= a.total) return;
+  const uint32_t cpr = (uint32_t)a.d / 8;
+  const uint32_t rh = i / cpr, c = i - rh * cpr;
+  const int64_t row = rh / a.hq;
+  const int h = (int)(rh - row * a.hq);
+  float M = -INFINITY;
+  for (int s = 0; s < a.ks; ++s) M = fmaxf(M, a.mpart[((int64_t)s * a.hq + h) * a.N + row]);
+  const float Mu = (M == -INFINITY) ? 0.f : M;
+  float l = 0.f;
+  f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < a.ks; ++s) {
+    const int64_t ml = ((int64_t)s * a.hq + h) * a.N + row;
+    const float ms = a.mpart[ml];
+    const float wgt = (ms == -INFINITY) ? 0.f : exp2f(ms - Mu);
+    l += wgt * a.lpart[ml];
+    const float *p = a.opart + (((int64_t)s * a.N + row) * a.hq + h) * a.d + c * 8;
+    o0 += wgt * *reinterpret_cast<const f32x4 *>(p);
+    o1 += wgt * *reinterpret_cast<const f32x4 *>(p + 4);
+  }
+  const float inv = 1.f / l;
+  u32x4 pk;
+  pk[0] = pack_bf16x2(o0[0] * inv, o0[1] * inv);
+  pk[1] = pack_bf16x2(o0[2] * inv, o0[3] * inv);
+  pk[2] = pack_bf16x2(o1[0] * inv, o1[1] * inv);
+  pk[3] = pack_bf16x2(o1[2] * inv, o1[3] * inv);
+  *reinterpret_cast<u32x4 *>(a.o + row * a.o_stride + (int64_t)h * a.d + c * 8) = pk;
+  if (c == 0) a.lse[(int64_t)h * a.N + row] = (M + log2f(l)) * kLn2;
+}
+
 template <int D, int HPW, int RB>
 int launch_fwd_cfg(FwdArgs a, hipStream_t stream) {
   using C = FwdCfg<D, HPW, RB>;
   a.nqb = (int)((a.N + C::BM - 1) / C::BM);
   a.nhg = a.hq / HPW;
-  const int64_t blocks = (int64_t)a.nqb * a.nhg;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, HPW, RB>), dim3((unsigned)blocks), dim3(C::NT), 0, stream, a);
+  a.qsplit = fwd_ksplit(a.N, a.hq, a.hq / a.G);
+  const int64_t blocks = (int64_t)a.nqb * a.nhg * a.qsplit;
+  if (a.qsplit > 1)
+    hipLaunchKernelGGL((attn_fwd_kernel<D, HPW, RB, true>), dim3((unsigned)blocks), dim3(C::NT), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<D, HPW, RB, false>), dim3((unsigned)blocks), dim3(C::NT), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_hip_error(e, "attn_fwd_kernel");
+  if (a.qsplit > 1) {
+    FwdMergeArgs m;
+    m.opart = a.opart;
+    m.mpart = a.mpart;
+    m.lpart = a.lpart;
+    m.o = a.o;
+    m.lse = a.lse;
+    m.N = a.N;
+    m.o_stride = a.o_stride;
+    m.hq = a.hq;
+    m.d = D;
+    m.ks = a.qsplit;
+    m.total = (uint32_t)(a.N * a.hq * D / 8);
+    hipLaunchKernelGGL(fwd_merge_kernel, dim3((m.total + 255) / 256), dim3(256), 0, stream, m);
+    e = hipGetLastError();
+    if (e != hipSuccess) return set_hip_error(e, "fwd_merge_kernel");
+  }
   return 0;
 }
 
@@ -314,6 +408,14 @@ int launch_attn_fwd(const AttnShape &s, const bf16_t *q, const bf16_t *k, const 
   a.cu = s.cu;
   a.n_seqs = s.n_seqs;
   a.nqb = a.nhg = 0;
+  {
+    const int ks = fwd_ksplit(s.N, s.hq, s.hkv);
+    float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + fwd_ws_part(s.N, s.hkv, s.d));
+    a.qsplit = 1;
+    a.opart = part;
+    a.mpart = part + (size_t)ks * s.N * s.hq * s.d;
+    a.lpart = a.mpart + (size_t)ks * s.hq * s.N;
+  }
   // Heads per workgroup: the largest of 4, 2, 1 dividing the group size, so
   // every workgroup reads a single KV head; 8 waves per workgroup.
   const int hpw = (a.G % 4 == 0) ? 4 : (a.G % 2 == 0) ? 2 : 1;

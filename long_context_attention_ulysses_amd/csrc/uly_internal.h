@@ -32,8 +32,31 @@ int launch_to_trans(const bf16_t *x, int64_t xs, int heads, int d, int64_t N, bf
                     hipStream_t stream);
 
 // Forward workspace: V^T [hkv][d][pad64(N)].
-inline size_t fwd_ws_bytes(int64_t N, int hkv, int d) {
+// Number of workgroups the forward splits each (query block of 256 / hpw
+// rows, group of hpw query heads) pair's key range over: 1 when there are at
+// least 512 pairs (two per CU), else enough to reach 512, at most 4; hpw is
+// the largest of 4, 2, 1 dividing the GQA group size. With a split the
+// kernel writes float32 partial softmax states (unnormalised O, running max,
+// sum) and a second pass merges them. The dq kernel uses the same blocks.
+inline int fwd_ksplit(int64_t N, int hq, int hkv) {
+  const int G = hq / hkv;
+  const int hpw = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+  const int64_t bm = 256 / hpw;
+  const int64_t pairs = (N + bm - 1) / bm * (hq / hpw);
+  if (pairs >= 512) return 1;
+  const int64_t s = (512 + pairs - 1) / pairs;
+  return s < 4 ? (int)s : 4;
+}
+
+// Forward workspace: V^T [hkv][d][pad64(N)] bf16, then, when the forward
+// splits its key ranges, float32 partials: O [s][N][hq][d], max [s][hq][N],
+// sum [s][hq][N].
+inline size_t fwd_ws_part(int64_t N, int hkv, int d) {
   return align256((size_t)hkv * d * pad64(N) * sizeof(bf16_t));
+}
+inline size_t fwd_ws_bytes(int64_t N, int hq, int hkv, int d) {
+  const int s = fwd_ksplit(N, hq, hkv);
+  return fwd_ws_part(N, hkv, d) + (s > 1 ? align256((size_t)s * N * hq * (d + 2) * 4) : 0);
 }
 
 // Number of workgroups the dK/dV kernel splits each (128-key block, KV head)
@@ -47,21 +70,10 @@ inline int dkdv_ksplit(int64_t N, int hkv) {
   return s < 4 ? (int)s : 4;
 }
 
-// Number of workgroups the dq kernel splits each (query block, head group)
-// pair's key range over: 1 when there are at least 512 pairs (two per CU),
-// else enough to reach 512, at most 4. The blocks are BM = 256 / hpw query
-// rows for hpw = 4, 2 or 1 heads per workgroup (the largest dividing the
-// GQA group size). With a split the kernel writes float32 partial dQ and a
-// second pass sums them.
-inline int dq_ksplit(int64_t N, int hq, int hkv) {
-  const int G = hq / hkv;
-  const int hpw = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
-  const int64_t bm = 256 / hpw;
-  const int64_t pairs = (N + bm - 1) / bm * (hq / hpw);
-  if (pairs >= 512) return 1;
-  const int64_t s = (512 + pairs - 1) / pairs;
-  return s < 4 ? (int)s : 4;
-}
+// The dq kernel splits its key ranges by the same rule as the forward
+// (same blocks); with a split it writes float32 partial dQ and a second
+// pass sums them.
+inline int dq_ksplit(int64_t N, int hq, int hkv) { return fwd_ksplit(N, hq, hkv); }
 
 // Backward workspace regions (byte offsets): D and LSE*log2(e) as float
 // [hq][pad64(N)], then K^T, Q^T, dO^T as contraction-ordered bf16 copies,
@@ -101,7 +113,7 @@ struct AttnShape {
   int n_seqs;
 };
 
-// ws: fwd_ws_bytes(N, hkv, d) bytes, 256-byte aligned.
+// ws: fwd_ws_bytes(N, hq, hkv, d) bytes, 256-byte aligned.
 int launch_attn_fwd(const AttnShape &s, const bf16_t *q, const bf16_t *k, const bf16_t *v,
                     bf16_t *o, float *lse, void *ws, hipStream_t stream);
 

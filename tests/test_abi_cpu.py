@@ -77,7 +77,7 @@ def test_swap_validation(args, code):
 
 def _fwd(**kw):
     a = dict(q=A, k=B, v=C, o=D_, lse=E, N=1024, hq=8, hkv=2, d=128, qs=1536, ks=1536, vs=1536,
-             os=1024, scale=0.088, causal=1, ws=W, wsb=1 << 24)
+             os=1024, scale=0.088, causal=1, ws=W, wsb=1 << 25)
     a.update(kw)
     return L.attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["N"], a["hq"], a["hkv"], a["d"], a["qs"],
                       a["ks"], a["vs"], a["os"], a["scale"], a["causal"], a["ws"], a["wsb"], None)
@@ -107,15 +107,17 @@ def test_attn_fwd_validation(kw, code):
 
 def test_attn_varlen_and_bwd_validation():
     r = L.attn_fwd_varlen(A, B, C, D_, E, 1024, 8, 2, 128, 1536, 1536, 1536, 1024, 0.1, 1, None, 3, 512,
-                          W, 1 << 24, None)
+                          W, 1 << 25, None)
     assert r == uly.CODE["ULY_E_NULL"]
     r = L.attn_fwd_varlen(A, B, C, D_, E, 1024, 8, 2, 128, 1536, 1536, 1536, 1024, 0.1, 1, F, 0, 512,
-                          W, 1 << 24, None)
+                          W, 1 << 25, None)
     assert r == uly.CODE["ULY_E_SHAPE"]
     N, hq, hkv, d = 1024, 8, 2, 128
     need = L.attn_bwd_workspace_bytes(N, hq, hkv, d, 1)
     assert need >= N * hq * 4 * 2 + N * d * (hkv + 2 * hq) * 2 and need % 256 == 0
-    assert L.attn_fwd_workspace_bytes(N, hq, hkv, d) == hkv * d * N * 2
+    # transposed V, plus float32 partial softmax states (O, max, sum) of the
+    # 4-way key split that 1024 tokens (32 query blocks x 2 head groups) get
+    assert L.attn_fwd_workspace_bytes(N, hq, hkv, d) == hkv * d * N * 2 + 4 * N * hq * (d + 2) * 4
 
     def bwd(ws=W, ws_bytes=need, dq=9 << 25, dk=10 << 25, dv=11 << 25):
         return L.attn_bwd(A, B, C, D_, E, F, dq, dk, dv, N, hq, hkv, d, 1536, 1536, 1536, 1024, 1024,
@@ -136,14 +138,18 @@ def test_workspaces_grow_linearly_with_n():
         for N in (4096, 65536, 262144):
             f1, f2 = L.attn_fwd_workspace_bytes(N, hq, hkv, d), L.attn_fwd_workspace_bytes(2 * N, hq, hkv, d)
             b1, b2 = L.attn_bwd_workspace_bytes(N, hq, hkv, d, 1), L.attn_bwd_workspace_bytes(2 * N, hq, hkv, d, 1)
-            assert f2 == 2 * f1
-            # below 256 (128-key block, KV head) pairs the dK/dV pass splits its
+            # below 512 (query block, head group) pairs the forward and the dq
+            # pass split their key ranges over up to 4 workgroups (float32
+            # partials); below 256 (128-key block, KV head) pairs the dK/dV pass splits its
             # query ranges, and below 512 (query block, head group) pairs the dq
             # pass splits its key ranges, over up to 4 workgroups each, keeping
             # float32 partials
             dkdv_split = N // 128 * hkv < 256
             dq_split = N // 64 * (hq // 4) < 512  # 4 heads per dq workgroup here
             split_max = (4 * N * hkv * 2 * d * 4 if dkdv_split else 0) + (4 * N * hq * d * 4 if dq_split else 0)
+            assert f1 <= hkv * d * N * 2 + (4 * N * hq * (d + 2) * 4 if dq_split else 0) + 512
+            if not dq_split:
+                assert f2 == 2 * f1
             assert b1 <= N * (2 * hq * 4 + (hkv + 2 * hq) * d * 2) + N // 64 * 4 + split_max + 2048
             if not dkdv_split and not dq_split:
                 assert abs(b2 - 2 * b1) <= 2048
