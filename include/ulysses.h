@@ -168,9 +168,9 @@ int attn_fwd_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v, uin
  * LSE*log2(e), [hq][roundup(N, 64)] each, then transposed copies of K, Q and
  * dO (hkv, hq and hq heads of d * roundup(N, 64) bf16), then an int32 array
  * of roundup(N, 64) / 64 entries (the varlen workgroup order of the dK/dV
- * pass), and, when there are fewer than 256 (128-key block, KV head) pairs,
+ * pass), and, when there are fewer than 512 (128-key block, KV head) pairs,
  * float32 partial dK/dV of s * N * hkv * 2 * d values, s = min(4,
- * ceil(256 / pairs)) (the dK/dV pass then splits each pair's queries over s
+ * ceil(512 / pairs)) (the dK/dV pass then splits each pair's queries over s
  * workgroups), and, when there are fewer than 512 (query block of 256 / hpw
  * rows, group of hpw query heads) pairs, hpw the largest of 4, 2, 1 dividing
  * hq / hkv, float32 partial dQ of s' * N * hq * d values, s' = min(4,

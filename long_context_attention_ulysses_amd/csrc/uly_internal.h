@@ -60,13 +60,13 @@ inline size_t fwd_ws_bytes(int64_t N, int hq, int hkv, int d) {
 }
 
 // Number of workgroups the dK/dV kernel splits each (128-key block, KV head)
-// pair's query range over: 1 when there are at least 256 pairs (one per CU
-// of the MI355X), else enough to reach 256, at most 4. With a split the
+// pair's query range over: 1 when there are at least 512 pairs (two per CU
+// of the MI355X), else enough to reach 512, at most 4. With a split the
 // kernel writes float32 partial dK/dV and a second pass sums them.
 inline int dkdv_ksplit(int64_t N, int hkv) {
   const int64_t pairs = (N + 127) / 128 * hkv;
-  if (pairs >= 256) return 1;
-  const int64_t s = (256 + pairs - 1) / pairs;
+  if (pairs >= 512) return 1;
+  const int64_t s = (512 + pairs - 1) / pairs;
   return s < 4 ? (int)s : 4;
 }
 

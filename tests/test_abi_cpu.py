@@ -140,11 +140,11 @@ def test_workspaces_grow_linearly_with_n():
             b1, b2 = L.attn_bwd_workspace_bytes(N, hq, hkv, d, 1), L.attn_bwd_workspace_bytes(2 * N, hq, hkv, d, 1)
             # below 512 (query block, head group) pairs the forward and the dq
             # pass split their key ranges over up to 4 workgroups (float32
-            # partials); below 256 (128-key block, KV head) pairs the dK/dV pass splits its
+            # partials); below 512 (128-key block, KV head) pairs the dK/dV pass splits its
             # query ranges, and below 512 (query block, head group) pairs the dq
             # pass splits its key ranges, over up to 4 workgroups each, keeping
             # float32 partials
-            dkdv_split = N // 128 * hkv < 256
+            dkdv_split = N // 128 * hkv < 512
             dq_split = N // 64 * (hq // 4) < 512  # 4 heads per dq workgroup here
             split_max = (4 * N * hkv * 2 * d * 4 if dkdv_split else 0) + (4 * N * hq * d * 4 if dq_split else 0)
             assert f1 <= hkv * d * N * 2 + (4 * N * hq * (d + 2) * 4 if dq_split else 0) + 512
