@@ -24,6 +24,10 @@
 //      (2-stage ring; concurrent workgroups walk the same tiles in step):
 //      S = Q K^T, dP = dO V^T (K, V in registers; a lane owns one key),
 //      P, dS, dV^T += dO^T P, dK^T += Q^T dS.
+// Small problems (fewer than 512 blocks of either kernel) split each block's
+// tiles over up to 4 workgroups that write float32 partials, summed in split
+// order by a second pass (still deterministic); over packed documents the
+// dkdv kernel takes its key blocks in order of decreasing work.
 #include <type_traits>
 
 #include "attn_common.h"

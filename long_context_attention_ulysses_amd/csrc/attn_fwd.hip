@@ -25,6 +25,10 @@
 //     causal mask), and consecutive workgroup ids alternate GQA groups, so the
 //     round-robin assignment of ids to the 8 XCDs keeps one KV head per XCD L2
 //     whenever the number of groups divides 8.
+//   * With fewer than 512 (query block, head group) pairs, each pair's key
+//     tiles are split over up to 4 workgroups that write their float32
+//     softmax states (unnormalised O, running max, sum); a merge pass combines
+//     them (exact: the states are rescaled to a common max).
 #include "attn_common.h"
 #include "uly_internal.h"
 
