@@ -405,7 +405,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU's share of the Ulysses path; runs on more than one GPU "
-              "are not part of this build (requested --gpus %d)" % args.gpus, file=sys.stderr)
+              "are not supported: the exchange between GPUs is not implemented (requested --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -23,7 +23,7 @@ STATUS = {
 CODE = {v: k for k, v in STATUS.items()}
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError("libulysses.so is not built (run `python -m long_context_attention_ulysses_amd.build`"
+    raise ImportError("libulysses.so is not built (run `python long_context_attention_ulysses_amd/build.py`"
                       " or __graft_entry__.build())")
 
 # torch ships its own HIP runtime with the same soname as /opt/rocm's. Load it
