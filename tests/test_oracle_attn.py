@@ -2,7 +2,7 @@
 
 Pinned to: PyTorch's CPU scaled_dot_product_attention and autograd in
 float64 (a library routine the definition reduces to), central finite
-differences, closed forms (Q = 0, constant V, constant K, first row) and
+differences, closed forms (Q = 0, K = 0, constant V, constant K, first row) and
 invariants (causality, documents, head-shard concatenation, GQA as repeated
 KV heads).
 """
@@ -130,6 +130,76 @@ def test_q_zero_closed_forms(cu):
         for g in range(hkv):
             ref = w[j:end, g * G:(g + 1) * G, :].sum(axis=(0, 1))
             np.testing.assert_allclose(dv[j, g], ref, rtol=1e-11, atol=1e-12)
+
+
+def _doc_bounds(N, cu):
+    """Start and end (exclusive) of the document holding each token."""
+    if cu is None:
+        return np.zeros(N, dtype=np.int64), np.full(N, N, dtype=np.int64)
+    cu = np.asarray(cu)
+    b = np.searchsorted(cu, np.arange(N), "right") - 1
+    return cu[b].astype(np.int64), cu[b + 1].astype(np.int64)
+
+
+@pytest.mark.parametrize("cu", [None, [0, 5, 6, 40, 64]])
+def test_q_zero_dq_closed_form(cu):
+    """Q = 0 makes every allowed score 0, so p_ij = 1/|A(i)| and
+    dQ_i = scale/|A(i)| * (sum_j (dO_i . v_j) k_j - D_i sum_j k_j), with
+    D_i = dO_i . mean_j v_j. The sums over j are prefix sums inside the
+    document: sum_j v_j k_j^T (a d x d matrix) and sum_j k_j."""
+    N, hq, hkv, d = 64, 4, 2, 8
+    G, scale = hq // hkv, 0.2
+    cu_a = None if cu is None else np.array(cu, dtype=np.int32)
+    q = np.zeros((N, hq, d))
+    k, v = _rand((N, hkv, d), 24), _rand((N, hkv, d), 25)
+    dout = _rand((N, hq, d), 26)
+    dq, _, _ = oracle.attn_bwd(q, k, v, dout, scale, True, cu_a)
+    start, _ = _doc_bounds(N, cu)
+    vk = np.cumsum(np.einsum("ngd,nge->ngde", v, k), axis=0)     # prefix sum of v_j k_j^T
+    ks, vs = np.cumsum(k, axis=0), np.cumsum(v, axis=0)
+    pre = lambda c, i: c[i] - (c[start[i] - 1] if start[i] > 0 else 0)  # noqa: E731
+    for i in range(N):
+        cnt = i - start[i] + 1
+        m_vk, s_k, s_v = pre(vk, i), pre(ks, i), pre(vs, i)
+        for h in range(hq):
+            g = h // G
+            dsum = dout[i, h] @ m_vk[g]                         # sum_j (dO_i . v_j) k_j
+            D = dout[i, h] @ (s_v[g] / cnt)
+            ref = scale / cnt * (dsum - D * s_k[g])
+            np.testing.assert_allclose(dq[i, h], ref, rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("cu", [None, [0, 9, 10, 33, 64]])
+def test_k_zero_closed_forms(cu):
+    """K = 0 also makes p_ij = 1/|A(i)|: dQ = 0, dV as for Q = 0, and
+    dK_j = scale * sum_{h in g} sum_{i sees j} (dO_i . v_j - D_i) q_i / |A(i)|,
+    i.e. suffix sums (inside the document) of q_i dO_i^T / |A(i)| applied to
+    v_j, minus suffix sums of D_i q_i / |A(i)|."""
+    N, hq, hkv, d = 64, 4, 2, 8
+    G, scale = hq // hkv, 0.3
+    cu_a = None if cu is None else np.array(cu, dtype=np.int32)
+    q, v = _rand((N, hq, d), 27), _rand((N, hkv, d), 28)
+    k = np.zeros((N, hkv, d))
+    dout = _rand((N, hq, d), 29)
+    dq, dk, dv = oracle.attn_bwd(q, k, v, dout, scale, True, cu_a)
+    assert np.max(np.abs(dq)) == 0.0
+    start, end = _doc_bounds(N, cu)
+    cnt = np.arange(N) - start + 1
+    vs = np.cumsum(v, axis=0)
+    mean_v = np.stack([(vs[i] - (vs[start[i] - 1] if start[i] > 0 else 0)) / cnt[i] for i in range(N)])
+    D = np.einsum("nhd,nhd->nh", dout, mean_v[:, np.arange(hq) // G])       # dO_i . o_i
+    w = 1.0 / cnt[:, None, None]
+    qdo = np.cumsum((np.einsum("nhd,nhe->nhde", q, dout) * w[..., None])[::-1], axis=0)[::-1]
+    dqs = np.cumsum((D[..., None] * q * w)[::-1], axis=0)[::-1]
+    dos = np.cumsum((dout * w)[::-1], axis=0)[::-1]
+    suf = lambda c, j: c[j] - (c[end[j]] if end[j] < N else 0)  # noqa: E731
+    for j in range(N):
+        s_qdo, s_dq, s_do = suf(qdo, j), suf(dqs, j), suf(dos, j)
+        for g in range(hkv):
+            hs = slice(g * G, (g + 1) * G)
+            ref_k = scale * ((s_qdo[hs] @ v[j, g]).sum(axis=0) - s_dq[hs].sum(axis=0))
+            np.testing.assert_allclose(dk[j, g], ref_k, rtol=1e-10, atol=1e-12)
+            np.testing.assert_allclose(dv[j, g], s_do[hs].sum(axis=0), rtol=1e-10, atol=1e-12)
 
 
 def test_constant_v_and_constant_k():
