@@ -1,6 +1,8 @@
 """GPU parity of attention forward/backward against the fp64 oracle, plus
 invariants checked on the GPU results themselves (determinism, causality,
 head-shard concatenation, single-document varlen == dense)."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -200,6 +202,25 @@ def test_workload_head_shard_sampled(name):
         assert_close(name + " dV[head]", oracle.bf16_to_f64(dv[:128]), dv_ref, GRAD_MAX_ABS, GRAD_REL)
     for t, nm in ((o, "O"), (dq, "dQ"), (dk, "dK"), (dv, "dV")):
         assert np.all(np.isfinite(oracle.bf16_to_f64(t))), nm + " has unwritten/non-finite elements"
+
+
+@pytest.mark.parametrize("name", [
+    "8k", "varlen",
+    pytest.param("64k", marks=pytest.mark.skipif(
+        os.environ.get("ULY_ORACLE_FULL") != "1",
+        reason="the full fp64 oracle at 64K takes about 10 minutes on 16 host threads; set ULY_ORACLE_FULL=1")),
+])
+def test_workload_head_shard_full_oracle(name):
+    """Rank 0's head shard at the workload's full size against the oracle on
+    every query row and every key: O, LSE, dQ, dK, dV. The oracle takes about
+    11 s at 8K and about a minute for the packed-document batch on 16 host
+    threads."""
+    w = workloads.WORKLOADS[name]
+    print("workload %s N=%d hq=%d hkv=%d (full oracle)" % (name, w.N, w.hq, w.hkv), flush=True)
+    qkv = workloads.gen_head_shard(w, 0)
+    dy = workloads.gen_dy_head_shard(w, 0)
+    cu = workloads.cu_seqlens(w) if w.varlen else None
+    _check_full(qkv, dy, w.hq, w.hkv, w.scale, True, cu, name)
 
 
 def test_q_zero_closed_form_full_size():
