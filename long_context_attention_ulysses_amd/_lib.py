@@ -97,14 +97,80 @@ def _check(rc: int, where: str):
         raise UlyssesError(rc, where)
 
 
-def _stream(stream) -> Optional[int]:
+def _stream(stream, device) -> int:
+    """The given stream, else torch's current stream on the tensors' device."""
     if stream is not None:
         return int(stream)
-    return torch.cuda.current_stream().cuda_stream
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
+
+
+_BITS16 = "bf16 bits (any 2-byte dtype)"
+
+
+class _Args:
+    """Checks the tensor arguments of one call for what the C interface
+    cannot see: every tensor is on the same GPU (a host pointer handed to a
+    kernel faults the device), has the element type the call reads, and,
+    where the call takes no strides, the shape and contiguity it assumes.
+    All checks run before the library is called."""
+
+    def __init__(self, where: str):
+        self.where = where
+        self.device = None
+
+    def __call__(self, t, name: str, kind=_BITS16, shape=None, contiguous: bool = False,
+                 min_numel: int = 0) -> int:
+        w = "%s: %s" % (self.where, name)
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch tensor" % w)
+        if not t.is_cuda:
+            raise ValueError("%s must be on a GPU" % w)
+        if self.device is None:
+            self.device = t.device
+        elif t.device != self.device:
+            raise ValueError("%s is on %s, the call's other tensors on %s" % (w, t.device, self.device))
+        if kind is _BITS16:
+            if t.element_size() != 2:
+                raise ValueError("%s must hold %s, got %s" % (w, _BITS16, t.dtype))
+        elif kind is not None and t.dtype != kind:
+            raise ValueError("%s must be %s, got %s" % (w, kind, t.dtype))
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError("%s must have shape %s, got %s" % (w, tuple(shape), tuple(t.shape)))
+        if contiguous and not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % w)
+        if t.numel() < min_numel:
+            raise ValueError("%s needs at least %d elements" % (w, min_numel))
+        return t.data_ptr()
+
+    def opt(self, t, name: str, **kw) -> Optional[int]:
+        return None if t is None else self(t, name, **kw)
+
+    def rows(self, t, name: str, N: int, heads: int, d: int) -> int:
+        """A [N, heads, d] view with unit element stride and head stride d
+        (any token stride): its token stride."""
+        self(t, name, shape=(N, heads, d))
+        return _tok_stride(t, heads, d)
+
+    def ws(self, t, name: str = "ws") -> int:
+        if t is None:
+            raise ValueError("%s: %s (device workspace) is required" % (self.where, name))
+        self(t, name, kind=None, contiguous=True)
+        return t.numel() * t.element_size()
+
+    def cu(self, t, N: int) -> int:
+        """cu_seqlens: contiguous int32 [n_seqs + 1] on the device; its values
+        are not read here (ulysses_check_cu_seqlens checks a host copy)."""
+        self(t, "cu_seqlens", kind=torch.int32, contiguous=True)
+        if t.dim() != 1 or t.numel() < 2 or t.numel() - 1 > N:
+            raise ValueError("%s: cu_seqlens must be 1-D with 2 to N + 1 entries" % self.where)
+        return t.numel() - 1
+
+    def stream(self, stream) -> int:
+        return _stream(stream, self.device)
 
 
 def status_string(status: int) -> str:
@@ -126,18 +192,37 @@ def _seg(seg_heads):
     return (_i32 * len(seg_heads))(*[int(s) for s in seg_heads])
 
 
+def _swap_shapes(where, x_seq, seg_heads):
+    if x_seq.dim() != 3:
+        raise ValueError("%s: the sequence-split tensor must be [n, H, d]" % where)
+    n, H, d = x_seq.shape
+    if sum(int(h) for h in seg_heads) != H:
+        raise ValueError("%s: segments %s do not add up to H = %d" % (where, list(seg_heads), H))
+    return n, H, d
+
+
 def ulysses_seq_to_head(x_seq, x_send, P: int, seg_heads: Sequence[int], stream=None) -> None:
     """x_seq [n, H, d] -> x_send [P, n, H/P, d] (contiguous 16-bit tensors)."""
-    n, H, d = x_seq.shape
-    _check(_L.ulysses_seq_to_head(_ptr(x_seq), _ptr(x_send), n, P, len(seg_heads), _seg(seg_heads), d,
-                                  _stream(stream)), "ulysses_seq_to_head")
+    a = _Args("ulysses_seq_to_head")
+    n, H, d = _swap_shapes(a.where, x_seq, seg_heads)
+    src = a(x_seq, "x_seq", contiguous=True)
+    dst = a(x_send, "x_send", contiguous=True)
+    if x_send.numel() != P * n * (H // P) * d:
+        raise ValueError("ulysses_seq_to_head: x_send must hold P * n * (H/P) * d elements")
+    _check(_L.ulysses_seq_to_head(src, dst, n, P, len(seg_heads), _seg(seg_heads), d, a.stream(stream)),
+           "ulysses_seq_to_head")
 
 
 def ulysses_head_to_seq(x_recv, x_seq, P: int, seg_heads: Sequence[int], stream=None) -> None:
     """x_recv [P, n, H/P, d] -> x_seq [n, H, d] (contiguous 16-bit tensors)."""
-    n, H, d = x_seq.shape
-    _check(_L.ulysses_head_to_seq(_ptr(x_recv), _ptr(x_seq), n, P, len(seg_heads), _seg(seg_heads), d,
-                                  _stream(stream)), "ulysses_head_to_seq")
+    a = _Args("ulysses_head_to_seq")
+    n, H, d = _swap_shapes(a.where, x_seq, seg_heads)
+    src = a(x_recv, "x_recv", contiguous=True)
+    dst = a(x_seq, "x_seq", contiguous=True)
+    if x_recv.numel() != P * n * (H // P) * d:
+        raise ValueError("ulysses_head_to_seq: x_recv must hold P * n * (H/P) * d elements")
+    _check(_L.ulysses_head_to_seq(src, dst, n, P, len(seg_heads), _seg(seg_heads), d, a.stream(stream)),
+           "ulysses_head_to_seq")
 
 
 def _tok_stride(t, heads, d):
@@ -155,80 +240,101 @@ def _workspace(nbytes: int, like):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=like.device)
 
 
+def _qkv_dims(q, k):
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q must be [N, hq, d] and k, v [N, hkv, d]")
+    N, hq, d = q.shape
+    return N, hq, k.shape[1], d
+
+
 def attn_fwd(q, k, v, o, lse, scale: float, causal: bool = True, cu_seqlens=None,
              max_seqlen: Optional[int] = None, ws=None, stream=None) -> None:
     """q [N, hq, d], k/v [N, hkv, d], o [N, hq, d] (views with any token stride);
     lse [hq, N] float32. cu_seqlens: int32 device tensor [n_seqs + 1] or None.
     ws: device buffer of at least attn_fwd_workspace_bytes(...) bytes (one is
     allocated when None)."""
-    N, hq, d = q.shape
-    hkv = k.shape[1]
+    a = _Args("attn_fwd" if cu_seqlens is None else "attn_fwd_varlen")
+    N, hq, hkv, d = _qkv_dims(q, k)
+    strides = (a.rows(q, "q", N, hq, d), a.rows(k, "k", N, hkv, d), a.rows(v, "v", N, hkv, d),
+               a.rows(o, "o", N, hq, d))
+    a(lse, "lse", kind=torch.float32, shape=(hq, N), contiguous=True)
+    n_seqs = a.cu(cu_seqlens, N) if cu_seqlens is not None else 0
     if ws is None:
         ws = _workspace(attn_fwd_workspace_bytes(N, hq, hkv, d), q)
-    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), N, hq, hkv, d, _tok_stride(q, hq, d),
-            _tok_stride(k, hkv, d), _tok_stride(v, hkv, d), _tok_stride(o, hq, d), float(scale), int(bool(causal)))
-    wsb = ws.numel() * ws.element_size()
+    wsb = a.ws(ws)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), N, hq, hkv, d) + strides + (float(scale),
+                                                                                        int(bool(causal)))
     if cu_seqlens is None:
-        _check(_L.attn_fwd(*args, _ptr(ws), wsb, _stream(stream)), "attn_fwd")
+        _check(_L.attn_fwd(*args, _ptr(ws), wsb, a.stream(stream)), "attn_fwd")
     else:
-        n_seqs = cu_seqlens.numel() - 1
         _check(_L.attn_fwd_varlen(*args, _ptr(cu_seqlens), n_seqs, int(max_seqlen or N), _ptr(ws), wsb,
-                                  _stream(stream)), "attn_fwd_varlen")
+                                  a.stream(stream)), "attn_fwd_varlen")
 
 
 def attn_bwd_workspace_bytes(N: int, hq: int, hkv: int, d: int, n_seqs: int = 1) -> int:
     return int(_L.attn_bwd_workspace_bytes(N, hq, hkv, d, n_seqs))
 
 
+def _bwd_args(a, q, k, v, o, lse, dout, N, hq, hkv, d):
+    """Pointers and token strides of the inputs every backward call reads."""
+    st = (a.rows(q, "q", N, hq, d), a.rows(k, "k", N, hkv, d), a.rows(v, "v", N, hkv, d))
+    st_o = a.rows(o, "o", N, hq, d) if o is not None else None
+    st_do = a.rows(dout, "dout", N, hq, d)
+    a(lse, "lse", kind=torch.float32, shape=(hq, N), contiguous=True)
+    return st, st_o, st_do
+
+
 def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, scale: float, causal: bool = True, ws=None,
              cu_seqlens=None, max_seqlen: Optional[int] = None, stream=None) -> None:
     """Gradients for attn_fwd with the same q, k, v, scale, mask. ws: device
     buffer of at least attn_bwd_workspace_bytes(...) bytes, 256-byte aligned."""
-    N, hq, d = q.shape
-    hkv = k.shape[1]
-    n_seqs = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    a = _Args("attn_bwd" if cu_seqlens is None else "attn_bwd_varlen")
+    N, hq, hkv, d = _qkv_dims(q, k)
+    st, st_o, st_do = _bwd_args(a, q, k, v, o, lse, dout, N, hq, hkv, d)
+    st_g = (a.rows(dq, "dq", N, hq, d), a.rows(dk, "dk", N, hkv, d), a.rows(dv, "dv", N, hkv, d))
+    n_seqs = a.cu(cu_seqlens, N) if cu_seqlens is not None else 1
     if ws is None:
         ws = _workspace(attn_bwd_workspace_bytes(N, hq, hkv, d, n_seqs), q)
-    ws_bytes = ws.numel() * ws.element_size()
+    ws_bytes = a.ws(ws)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
-            N, hq, hkv, d, _tok_stride(q, hq, d), _tok_stride(k, hkv, d), _tok_stride(v, hkv, d),
-            _tok_stride(o, hq, d), _tok_stride(dout, hq, d), _tok_stride(dq, hq, d), _tok_stride(dk, hkv, d),
-            _tok_stride(dv, hkv, d), float(scale), int(bool(causal)))
+            N, hq, hkv, d) + st + (st_o, st_do) + st_g + (float(scale), int(bool(causal)))
     if cu_seqlens is None:
-        _check(_L.attn_bwd(*args, _ptr(ws), ws_bytes, _stream(stream)), "attn_bwd")
+        _check(_L.attn_bwd(*args, _ptr(ws), ws_bytes, a.stream(stream)), "attn_bwd")
     else:
         _check(_L.attn_bwd_varlen(*args, _ptr(cu_seqlens), n_seqs, int(max_seqlen or N), _ptr(ws), ws_bytes,
-                                  _stream(stream)), "attn_bwd_varlen")
+                                  a.stream(stream)), "attn_bwd_varlen")
 
 
 def attn_bwd_dq(q, k, v, o, lse, dout, dq, scale: float, causal: bool = True, ws=None, cu_seqlens=None,
                 stream=None) -> None:
     """First step of attn_bwd: D = rowsum(dout * o) into ws, and dq."""
-    N, hq, d = q.shape
-    hkv = k.shape[1]
-    n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    a = _Args("attn_bwd_dq")
+    N, hq, hkv, d = _qkv_dims(q, k)
+    st, st_o, st_do = _bwd_args(a, q, k, v, o, lse, dout, N, hq, hkv, d)
+    st_dq = a.rows(dq, "dq", N, hq, d)
+    n_seqs = a.cu(cu_seqlens, N) if cu_seqlens is not None else 0
+    ws_bytes = a.ws(ws)
     _check(_L.attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), N, hq, hkv, d,
-                          _tok_stride(q, hq, d), _tok_stride(k, hkv, d), _tok_stride(v, hkv, d),
-                          _tok_stride(o, hq, d), _tok_stride(dout, hq, d), _tok_stride(dq, hq, d), float(scale),
-                          int(bool(causal)), _ptr(cu_seqlens), n_seqs, _ptr(ws), ws.numel() * ws.element_size(),
-                          _stream(stream)), "attn_bwd_dq")
+                          *st, st_o, st_do, st_dq, float(scale), int(bool(causal)), _ptr(cu_seqlens), n_seqs,
+                          _ptr(ws), ws_bytes, a.stream(stream)), "attn_bwd_dq")
 
 
 def attn_bwd_dkdv(q, k, v, lse, dout, dk, dv, scale: float, causal: bool = True, ws=None, cu_seqlens=None,
                   stream=None) -> None:
     """Second step of attn_bwd: dk and dv, reading D from ws (left by attn_bwd_dq)."""
-    N, hq, d = q.shape
-    hkv = k.shape[1]
-    n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    a = _Args("attn_bwd_dkdv")
+    N, hq, hkv, d = _qkv_dims(q, k)
+    st, _, st_do = _bwd_args(a, q, k, v, None, lse, dout, N, hq, hkv, d)
+    st_kv = (a.rows(dk, "dk", N, hkv, d), a.rows(dv, "dv", N, hkv, d))
+    n_seqs = a.cu(cu_seqlens, N) if cu_seqlens is not None else 0
+    ws_bytes = a.ws(ws)
     _check(_L.attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(dk), _ptr(dv), N, hq, hkv, d,
-                            _tok_stride(q, hq, d), _tok_stride(k, hkv, d), _tok_stride(v, hkv, d),
-                            _tok_stride(dout, hq, d), _tok_stride(dk, hkv, d), _tok_stride(dv, hkv, d),
-                            float(scale), int(bool(causal)), _ptr(cu_seqlens), n_seqs, _ptr(ws),
-                            ws.numel() * ws.element_size(), _stream(stream)), "attn_bwd_dkdv")
+                            *st, st_do, *st_kv, float(scale), int(bool(causal)), _ptr(cu_seqlens), n_seqs,
+                            _ptr(ws), ws_bytes, a.stream(stream)), "attn_bwd_dkdv")
 
 
-def _ptr_array(ts):
-    return (_p * len(ts))(*[t.data_ptr() for t in ts])
+def _ptr_array(ptrs):
+    return (_p * len(ptrs))(*ptrs)
 
 
 def attn_lse_merge(o_parts, lse_parts, o_out, lse_out, stream=None) -> None:
@@ -237,13 +343,20 @@ def attn_lse_merge(o_parts, lse_parts, o_out, lse_out, stream=None) -> None:
     o_out [N, h, d], lse_out [h, N]."""
     if len(o_parts) != len(lse_parts) or not o_parts:
         raise ValueError("need as many lse parts as o parts, at least one")
+    a = _Args("attn_lse_merge")
+    if o_out.dim() != 3:
+        raise ValueError("attn_lse_merge: o_out must be [N, h, d]")
     N, h, d = o_out.shape
-    strides = {_tok_stride(t, h, d) for t in o_parts}
-    if len(strides) != 1 or any(tuple(t.shape) != (N, h, d) for t in o_parts):
-        raise ValueError("o parts must share one shape and token stride")
-    _check(_L.attn_lse_merge(len(o_parts), _ptr_array(o_parts), _ptr_array(lse_parts), _ptr(o_out),
-                             _ptr(lse_out), N, h, d, strides.pop(), _tok_stride(o_out, h, d), _stream(stream)),
-           "attn_lse_merge")
+    strides = {a.rows(t, "o_parts[%d]" % i, N, h, d) for i, t in enumerate(o_parts)}
+    if len(strides) != 1:
+        raise ValueError("o parts must share one token stride")
+    lp = [a(t, "lse_parts[%d]" % i, kind=torch.float32, shape=(h, N), contiguous=True)
+          for i, t in enumerate(lse_parts)]
+    op = [t.data_ptr() for t in o_parts]
+    out_stride = a.rows(o_out, "o_out", N, h, d)
+    a(lse_out, "lse_out", kind=torch.float32, shape=(h, N), contiguous=True)
+    _check(_L.attn_lse_merge(len(o_parts), _ptr_array(op), _ptr_array(lp), _ptr(o_out), _ptr(lse_out), N, h, d,
+                             strides.pop(), out_stride, a.stream(stream)), "attn_lse_merge")
 
 
 def ring_grad_sum(parts, out, stream=None) -> None:
@@ -251,12 +364,16 @@ def ring_grad_sum(parts, out, stream=None) -> None:
     stride), accumulated in float32."""
     if not parts:
         raise ValueError("need at least one part")
+    a = _Args("ring_grad_sum")
+    if out.dim() != 3:
+        raise ValueError("ring_grad_sum: out must be [rows, heads, d]")
     rows, heads, d = out.shape
-    strides = {_tok_stride(t, heads, d) for t in parts}
-    if len(strides) != 1 or any(tuple(t.shape) != (rows, heads, d) for t in parts):
-        raise ValueError("parts must share one shape and token stride")
-    _check(_L.ring_grad_sum(len(parts), _ptr_array(parts), _ptr(out), rows, heads * d, strides.pop(),
-                            _tok_stride(out, heads, d), _stream(stream)), "ring_grad_sum")
+    strides = {a.rows(t, "parts[%d]" % i, rows, heads, d) for i, t in enumerate(parts)}
+    if len(strides) != 1:
+        raise ValueError("parts must share one token stride")
+    out_stride = a.rows(out, "out", rows, heads, d)
+    _check(_L.ring_grad_sum(len(parts), _ptr_array([t.data_ptr() for t in parts]), _ptr(out), rows, heads * d,
+                            strides.pop(), out_stride, a.stream(stream)), "ring_grad_sum")
 
 
 def _row_stride(t, V):
@@ -269,9 +386,18 @@ def shifted_ce_fwd(logits, labels, row_loss, row_lse, loss_out, good_out, stream
     """Per-rank loss from pre-shifted labels: logits [n, V] bf16 bits,
     labels [n] int32 (-100 = no loss); outputs row_loss, row_lse [n] float32,
     loss_out [1] float32 (mean over good rows), good_out [1] int32."""
+    a = _Args("shifted_ce_fwd")
+    if logits.dim() != 2:
+        raise ValueError("shifted_ce_fwd: logits must be [n, V]")
     n, V = logits.shape
+    a(logits, "logits")
+    a(labels, "labels", kind=torch.int32, shape=(n,), contiguous=True)
+    a(row_loss, "row_loss", kind=torch.float32, shape=(n,), contiguous=True)
+    a(row_lse, "row_lse", kind=torch.float32, shape=(n,), contiguous=True)
+    a(loss_out, "loss_out", kind=torch.float32, min_numel=1)
+    a(good_out, "good_out", kind=torch.int32, min_numel=1)
     _check(_L.shifted_ce_fwd(_ptr(logits), _ptr(labels), n, V, _row_stride(logits, V), _ptr(row_loss),
-                             _ptr(row_lse), _ptr(loss_out), _ptr(good_out), _stream(stream)), "shifted_ce_fwd")
+                             _ptr(row_lse), _ptr(loss_out), _ptr(good_out), a.stream(stream)), "shifted_ce_fwd")
 
 
 def sp_loss_aggregate(rank_losses, rank_goods, total_out, row_grad_scale_out, stream=None) -> None:
@@ -279,16 +405,29 @@ def sp_loss_aggregate(rank_losses, rank_goods, total_out, row_grad_scale_out, st
     scalars, and the per-row gradient scale 1 / max(sum_r good_r, 1)."""
     if len(rank_losses) != len(rank_goods) or not rank_losses:
         raise ValueError("need one good count per rank loss, at least one rank")
-    _check(_L.sp_loss_aggregate(len(rank_losses), _ptr_array(rank_losses), _ptr_array(rank_goods),
-                                _ptr(total_out), _ptr(row_grad_scale_out), _stream(stream)), "sp_loss_aggregate")
+    a = _Args("sp_loss_aggregate")
+    lp = [a(t, "rank_losses[%d]" % i, kind=torch.float32, min_numel=1) for i, t in enumerate(rank_losses)]
+    gp = [a(t, "rank_goods[%d]" % i, kind=torch.int32, min_numel=1) for i, t in enumerate(rank_goods)]
+    a(total_out, "total_out", kind=torch.float32, min_numel=1)
+    a(row_grad_scale_out, "row_grad_scale_out", kind=torch.float32, min_numel=1)
+    _check(_L.sp_loss_aggregate(len(rank_losses), _ptr_array(lp), _ptr_array(gp), _ptr(total_out),
+                                _ptr(row_grad_scale_out), a.stream(stream)), "sp_loss_aggregate")
 
 
 def shifted_ce_bwd(logits, labels, row_lse, row_grad_scale, dlogits, stream=None) -> None:
     """Gradient of the aggregate loss with respect to one rank's logits
     (dlogits may be logits itself)."""
+    a = _Args("shifted_ce_bwd")
+    if logits.dim() != 2:
+        raise ValueError("shifted_ce_bwd: logits must be [n, V]")
     n, V = logits.shape
+    a(logits, "logits")
+    a(labels, "labels", kind=torch.int32, shape=(n,), contiguous=True)
+    a(row_lse, "row_lse", kind=torch.float32, shape=(n,), contiguous=True)
+    a(row_grad_scale, "row_grad_scale", kind=torch.float32, min_numel=1)
+    a(dlogits, "dlogits", shape=(n, V))
     _check(_L.shifted_ce_bwd(_ptr(logits), _ptr(labels), _ptr(row_lse), _ptr(row_grad_scale), n, V,
-                             _row_stride(logits, V), _ptr(dlogits), _row_stride(dlogits, V), _stream(stream)),
+                             _row_stride(logits, V), _ptr(dlogits), _row_stride(dlogits, V), a.stream(stream)),
            "shifted_ce_bwd")
 
 
@@ -296,35 +435,39 @@ def tiled_mlp_workspace_bytes(tile: int, H: int, I: int) -> int:
     return int(_L.tiled_mlp_workspace_bytes(tile, H, I))
 
 
-def _contig(t, shape):
-    if tuple(t.shape) != tuple(shape) or not t.is_contiguous():
-        raise ValueError("expected a contiguous tensor of shape %s" % (tuple(shape),))
-
-
 def tiled_mlp_fwd(x, w_gu, w_down, y, tile: int, ws=None, stream=None) -> None:
     """y [n, H] = SwiGLU MLP of x [n, H] with w_gu [2I, H], w_down [H, I]
     (bf16 bits), over token tiles of `tile`."""
+    a = _Args("tiled_mlp_fwd")
+    if x.dim() != 2 or w_down.dim() != 2:
+        raise ValueError("tiled_mlp_fwd: x must be [n, H] and w_down [H, I]")
     n, H = x.shape
     I = w_down.shape[1]
-    for t, s in ((x, (n, H)), (w_gu, (2 * I, H)), (w_down, (H, I)), (y, (n, H))):
-        _contig(t, s)
+    for t, nm, sh in ((x, "x", (n, H)), (w_gu, "w_gu", (2 * I, H)), (w_down, "w_down", (H, I)), (y, "y", (n, H))):
+        a(t, nm, shape=sh, contiguous=True)
     if ws is None:
         ws = _workspace(tiled_mlp_workspace_bytes(tile, H, I), x)
-    _check(_L.tiled_mlp_fwd(_ptr(x), _ptr(w_gu), _ptr(w_down), _ptr(y), n, H, I, tile, _ptr(ws),
-                            ws.numel() * ws.element_size(), _stream(stream)), "tiled_mlp_fwd")
+    wsb = a.ws(ws)
+    _check(_L.tiled_mlp_fwd(_ptr(x), _ptr(w_gu), _ptr(w_down), _ptr(y), n, H, I, tile, _ptr(ws), wsb,
+                            a.stream(stream)), "tiled_mlp_fwd")
 
 
 def tiled_mlp_bwd(x, w_gu, w_down, dy, dx, dw_gu, dw_down, tile: int, accumulate: bool = False, ws=None,
                   stream=None) -> None:
     """dx [n, H] (bf16) and the float32 weight gradients dw_gu [2I, H],
     dw_down [H, I] of the SwiGLU MLP, recomputing each tile's activations."""
+    a = _Args("tiled_mlp_bwd")
+    if x.dim() != 2 or w_down.dim() != 2:
+        raise ValueError("tiled_mlp_bwd: x must be [n, H] and w_down [H, I]")
     n, H = x.shape
     I = w_down.shape[1]
-    for t, s in ((x, (n, H)), (w_gu, (2 * I, H)), (w_down, (H, I)), (dy, (n, H)), (dx, (n, H)),
-                 (dw_gu, (2 * I, H)), (dw_down, (H, I))):
-        _contig(t, s)
+    for t, nm, sh in ((x, "x", (n, H)), (w_gu, "w_gu", (2 * I, H)), (w_down, "w_down", (H, I)), (dy, "dy", (n, H)),
+                      (dx, "dx", (n, H))):
+        a(t, nm, shape=sh, contiguous=True)
+    a(dw_gu, "dw_gu", kind=torch.float32, shape=(2 * I, H), contiguous=True)
+    a(dw_down, "dw_down", kind=torch.float32, shape=(H, I), contiguous=True)
     if ws is None:
         ws = _workspace(tiled_mlp_workspace_bytes(tile, H, I), x)
+    wsb = a.ws(ws)
     _check(_L.tiled_mlp_bwd(_ptr(x), _ptr(w_gu), _ptr(w_down), _ptr(dy), _ptr(dx), _ptr(dw_gu), _ptr(dw_down), n,
-                            H, I, tile, int(bool(accumulate)), _ptr(ws), ws.numel() * ws.element_size(),
-                            _stream(stream)), "tiled_mlp_bwd")
+                            H, I, tile, int(bool(accumulate)), _ptr(ws), wsb, a.stream(stream)), "tiled_mlp_bwd")

@@ -153,3 +153,22 @@ def test_workspaces_grow_linearly_with_n():
             assert b1 <= N * (2 * hq * 4 + (hkv + 2 * hq) * d * 2) + N // 64 * 4 + split_max + 2048
             if not dkdv_split and not dq_split:
                 assert abs(b2 - 2 * b1) <= 2048
+
+
+def test_binding_rejects_host_tensors():
+    """The binding refuses tensors that are not on a GPU before calling the
+    library: a host pointer handed to a kernel would fault the device."""
+    import torch
+    import long_context_attention_ulysses_amd as uly
+    x = torch.zeros((8, 4, 16), dtype=torch.int16)
+    out = torch.zeros((2, 8, 2, 16), dtype=torch.int16)
+    with pytest.raises(ValueError, match="must be on a GPU"):
+        uly.ulysses_seq_to_head(x, out, 2, [4])
+    q = torch.zeros((64, 4, 64), dtype=torch.int16)
+    k = torch.zeros((64, 2, 64), dtype=torch.int16)
+    lse = torch.zeros((4, 64), dtype=torch.float32)
+    ws = torch.zeros((1 << 20,), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="must be on a GPU"):
+        uly.attn_fwd(q, k, k, q.clone(), lse, 0.125, ws=ws)
+    with pytest.raises(TypeError):
+        uly.ring_grad_sum([q.numpy()], q)

@@ -324,6 +324,21 @@ def test_attention_argument_errors():
     with pytest.raises(uly.UlyssesError) as e:
         uly.attn_fwd(q, q[:, :2], q[:, :2], q, lse, 0.1)      # o aliases q
     assert e.value.name == "ULY_E_ALIAS"
+    # caught by the binding before the library is called: what the C
+    # interface cannot see (sizes of the buffers behind the pointers, dtypes)
+    k2 = torch.zeros((64, 2, 128), dtype=torch.int16, device="cuda")
+    with pytest.raises(ValueError):
+        uly.attn_fwd(q, k2[:32], k2, o, lse, 0.1)              # k shorter than N
+    with pytest.raises(ValueError):
+        uly.attn_fwd(q, k2, k2, o, lse[:, :32], 0.1)           # lse too small
+    with pytest.raises(ValueError):
+        uly.attn_fwd(q, k2, k2, o, lse.double(), 0.1)          # lse not float32
+    with pytest.raises(ValueError):
+        uly.attn_fwd(q.float(), k2, k2, o, lse, 0.1)           # 4-byte elements
+    with pytest.raises(ValueError):
+        uly.attn_fwd(q, k2, k2, o, lse, 0.1, cu_seqlens=torch.tensor([0, 64], device="cuda"))  # int64
+    with pytest.raises(ValueError):
+        uly.attn_bwd_dq(q, k2, k2, o, lse, q, o, 0.1)          # no workspace
     torch.cuda.synchronize()
     assert np.all(host(o) == 0xFFFF)
 

@@ -125,6 +125,11 @@ def test_loss_argument_errors():
     with pytest.raises(uly.UlyssesError) as e:
         uly.sp_loss_aggregate([s] * 17, [gi] * 17, s.clone(), s.clone())
     assert e.value.name == "ULY_E_SHAPE"
+    big = torch.zeros((n + 1, V), dtype=torch.int16, device="cuda")
     with pytest.raises(uly.UlyssesError) as e:
-        uly.shifted_ce_bwd(x, lab, f, s, x[1:])                      # partial overlap
+        uly.shifted_ce_bwd(big[:n], lab, f, s, big[1:])              # partial overlap
     assert e.value.name == "ULY_E_ALIAS"
+    with pytest.raises(ValueError):
+        uly.shifted_ce_bwd(x, lab, f, s, big[2:])                    # dlogits one row short
+    with pytest.raises(ValueError):
+        uly.shifted_ce_fwd(x, lab.float(), f, f2, s, gi)             # labels must be int32

@@ -86,5 +86,14 @@ def test_swap_errors_leave_output_untouched():
     with pytest.raises(uly.UlyssesError) as e:
         uly.ulysses_seq_to_head(x, x, 2, [2, 4])            # in place
     assert e.value.name == "ULY_E_ALIAS"
+    out2 = sentinel((2, 8, 3, 16))
+    with pytest.raises(ValueError):
+        uly.ulysses_seq_to_head(x.transpose(0, 1).contiguous().transpose(0, 1), out2, 2, [2, 4])  # not contiguous
+    with pytest.raises(ValueError):
+        uly.ulysses_seq_to_head(x, out2[:1], 2, [2, 4])      # output too small
+    with pytest.raises(ValueError):
+        uly.ulysses_seq_to_head(x, out2, 2, [2, 2])          # segments do not add up to H
+    torch.cuda.synchronize()
+    assert np.all(host(out2) == 0xFFFF)
     torch.cuda.synchronize()
     assert np.all(host(out) == 0xFFFF)
