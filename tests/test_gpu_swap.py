@@ -41,6 +41,10 @@ def _unpack(r_bits, P, segs):
     # token-major kernel's index-table limit
     (37, 4, [256, 64, 64], 128),
     (9, 8, [128, 64, 64], 128),
+    # rows past the table limit with more (chunk, segment) runs than one
+    # launch of the run-major kernel takes (48 and 96 runs: 2 and 3 launches)
+    (3, 16, [256, 64, 64], 128),
+    (2, 32, [256, 64, 64], 128),
 ])
 def test_swap_small_shapes_bit_exact(n, P, segs, d):
     x = workloads.normal_bf16((n, sum(segs), d), seed=n * 131 + P)
