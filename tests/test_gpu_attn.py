@@ -223,6 +223,37 @@ def test_workload_head_shard_full_oracle(name):
     _check_full(qkv, dy, w.hq, w.hkv, w.scale, True, cu, name)
 
 
+@pytest.mark.parametrize("N,hq,hkv,d", [
+    (16384, 8, 4, 128),   # G = 2: two heads per workgroup
+    (65536, 3, 1, 128),   # G = 3: one head per workgroup
+    (32768, 8, 2, 64),    # d = 64
+])
+def test_unsplit_grids_sampled(N, hq, hkv, d):
+    """Problems large enough that no kernel splits its ranges (at least 512
+    blocks per grid), for the head-group sizes and head dim the workloads
+    above do not reach unsplit; oracle on sampled query rows and the last
+    128 keys."""
+    print("unsplit N=%d hq=%d hkv=%d d=%d" % (N, hq, hkv, d), flush=True)
+    qkv = workloads.normal_bf16((N, hq + 2 * hkv, d), seed=N + hq * 7 + d, sigma=0.5)
+    dy = workloads.normal_bf16((N, hq, d), seed=N + hq * 11 + d)
+    scale = 1.0 / np.sqrt(d)
+    r = Run(qkv, hq, hkv, scale)
+    o, lse = r.fwd()
+    dq, dk, dv = r.bwd(dy)
+    q, k, v = _split(qkv, hq, hkv)
+    rows = _sample_rows(N, N // 4, 48, seed=N % 97 + hq)
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, scale, True, None, rows=rows)
+    assert_close("O[rows]", oracle.bf16_to_f64(o[rows]), o_ref, FWD_MAX_ABS, FWD_REL)
+    assert_close("LSE[rows]", lse[:, rows].astype(np.float64), lse_ref, LSE_MAX_ABS, 1.0)
+    klo = N - 128
+    dq_ref, dk_ref, dv_ref = oracle.attn_bwd(q, k, v, dy, scale, True, None, rows=rows, key_lo=klo)
+    assert_close("dQ[rows]", oracle.bf16_to_f64(dq[rows]), dq_ref, GRAD_MAX_ABS, GRAD_REL)
+    assert_close("dK[tail]", oracle.bf16_to_f64(dk[klo:]), dk_ref, GRAD_MAX_ABS, GRAD_REL)
+    assert_close("dV[tail]", oracle.bf16_to_f64(dv[klo:]), dv_ref, GRAD_MAX_ABS, GRAD_REL)
+    for t, nm in ((o, "O"), (dq, "dQ"), (dk, "dK"), (dv, "dV")):
+        assert np.all(np.isfinite(oracle.bf16_to_f64(t))), nm + " has unwritten/non-finite elements"
+
+
 def test_q_zero_closed_form_full_size():
     """Q = 0 at 64K: o_i = mean(v_0..v_i), LSE_i = ln(i+1) for every row, and
     dK = 0 exactly (checked over all N rows via prefix sums)."""
