@@ -254,6 +254,42 @@ def test_unsplit_grids_sampled(N, hq, hkv, d):
         assert np.all(np.isfinite(oracle.bf16_to_f64(t))), nm + " has unwritten/non-finite elements"
 
 
+def test_long_packed_batch_sampled():
+    """2.1 M tokens in short documents: more key blocks than the dK/dV
+    kernel's work sort takes (it keeps key order then), grids of over 16000
+    workgroups and the largest row offsets the tests reach; oracle on sampled
+    rows and on the first and last 128 keys."""
+    N, hq, hkv, d = 2_100_000, 2, 1, 64
+    rng = np.random.default_rng(0x10C)
+    lens = []
+    while sum(lens) < N:
+        lens.append(int(rng.integers(1, 1201)))
+    lens[-1] -= sum(lens) - N
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    print("long packed batch N=%d docs=%d" % (N, len(lens)), flush=True)
+    qkv = workloads.normal_bf16((N, hq + 2 * hkv, d), seed=0x10D, sigma=0.5)
+    dy = workloads.normal_bf16((N, hq, d), seed=0x10E)
+    scale = 1.0 / np.sqrt(d)
+    r = Run(qkv, hq, hkv, scale, True, cu)
+    o, lse = r.fwd()
+    dq, dk, dv = r.bwd(dy)
+    q, k, v = _split(qkv, hq, hkv)
+    rows = np.unique(np.concatenate([_sample_rows(N, N // 4, 64, seed=3), cu[-4:-1], cu[-4:-1] - 1]))
+    rows = rows[(rows >= 0) & (rows < N)]
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, scale, True, cu, rows=rows)
+    assert_close("O[rows]", oracle.bf16_to_f64(o[rows]), o_ref, FWD_MAX_ABS, FWD_REL)
+    assert_close("LSE[rows]", lse[:, rows].astype(np.float64), lse_ref, LSE_MAX_ABS, 1.0)
+    dq_ref, _, _ = oracle.attn_bwd(q, k, v, dy, scale, True, cu, rows=rows, want_dkv=False)
+    assert_close("dQ[rows]", oracle.bf16_to_f64(dq[rows]), dq_ref, GRAD_MAX_ABS, GRAD_REL)
+    for lo, hi in ((0, 128), (N - 128, N)):
+        _, dk_ref, dv_ref = oracle.attn_bwd(q, k, v, dy, scale, True, cu, rows=rows[:1], key_lo=lo, key_hi=hi,
+                                            want_dq=False)
+        assert_close("dK[%d:%d]" % (lo, hi), oracle.bf16_to_f64(dk[lo:hi]), dk_ref, GRAD_MAX_ABS, GRAD_REL)
+        assert_close("dV[%d:%d]" % (lo, hi), oracle.bf16_to_f64(dv[lo:hi]), dv_ref, GRAD_MAX_ABS, GRAD_REL)
+    for t, nm in ((o, "O"), (dq, "dQ"), (dk, "dK"), (dv, "dV")):  # bf16 exponent all ones: NaN or Inf
+        assert not np.any((t & 0x7F80) == 0x7F80), nm + " has unwritten/non-finite elements"
+
+
 def test_q_zero_closed_form_full_size():
     """Q = 0 at 64K: o_i = mean(v_0..v_i), LSE_i = ln(i+1) for every row, and
     dK = 0 exactly (checked over all N rows via prefix sums)."""
