@@ -290,6 +290,32 @@ def test_long_packed_batch_sampled():
         assert not np.any((t & 0x7F80) == 0x7F80), nm + " has unwritten/non-finite elements"
 
 
+def test_separate_and_strided_layouts_give_identical_bits():
+    """The kernels see only pointers and token strides: separate contiguous
+    q, k, v and dq, dk, dv tensors, and an output that is a view inside a
+    wider buffer, give the same bits as the fused q|k|v layout."""
+    N, hq, hkv, d = 777, 4, 2, 128
+    qkv = workloads.normal_bf16((N, hq + 2 * hkv, d), seed=606, sigma=0.5)
+    dy = workloads.normal_bf16((N, hq, d), seed=607)
+    scale = 1.0 / np.sqrt(d)
+    fused = Run(qkv, hq, hkv, scale)
+    o1, l1 = fused.fwd()
+    g1 = fused.bwd(dy)
+    qs, ks, vs = (dev(np.ascontiguousarray(x)) for x in _split(qkv, hq, hkv))
+    wide = sentinel((N, hq + 2, d))
+    o2 = wide[:, 1:1 + hq]                      # token stride (hq + 2) * d, offset d
+    lse2 = torch.empty((hq, N), dtype=torch.float32, device="cuda")
+    uly.attn_fwd(qs, ks, vs, o2, lse2, scale, True)
+    dq2, dk2, dv2 = sentinel((N, hq, d)), sentinel((N, hkv, d)), sentinel((N, hkv, d))
+    ws = torch.empty(uly.attn_bwd_workspace_bytes(N, hq, hkv, d), dtype=torch.uint8, device="cuda")
+    uly.attn_bwd(qs, ks, vs, o2, lse2, dev(dy), dq2, dk2, dv2, scale, True, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(o2), o1) and np.array_equal(lse2.cpu().numpy(), l1)
+    assert np.all(host(wide[:, 0]) == 0xFFFF) and np.all(host(wide[:, 1 + hq]) == 0xFFFF)  # untouched
+    for a, b in zip((host(dq2), host(dk2), host(dv2)), g1):
+        assert np.array_equal(a, b)
+
+
 def test_q_zero_closed_form_full_size():
     """Q = 0 at 64K: o_i = mean(v_0..v_i), LSE_i = ln(i+1) for every row, and
     dK = 0 exactly (checked over all N rows via prefix sums)."""
