@@ -26,10 +26,10 @@ class Layer:
     for what the exchange would bring), attention forward and backward,
     unpack O and dq|dk|dv."""
 
-    def __init__(self):
-        self.x = dev(workloads.normal_bf16((n, Ht, d), seed=71, sigma=0.5))
-        self.shard = dev(workloads.normal_bf16((N, ht, d), seed=72, sigma=0.5))
-        self.dy = dev(workloads.normal_bf16((N, hq, d), seed=73))
+    def __init__(self, seed=71):
+        self.x = dev(workloads.normal_bf16((n, Ht, d), seed=seed, sigma=0.5))
+        self.shard = dev(workloads.normal_bf16((N, ht, d), seed=seed + 1, sigma=0.5))
+        self.dy = dev(workloads.normal_bf16((N, hq, d), seed=seed + 2))
         self.send = torch.empty((P, n, ht, d), dtype=torch.int16, device="cuda")
         self.o = torch.empty((N, hq, d), dtype=torch.int16, device="cuda")
         self.lse = torch.empty((hq, N), dtype=torch.float32, device="cuda")
@@ -94,3 +94,26 @@ def test_layer_captured_in_a_hip_graph_replays_exactly():
         torch.cuda.synchronize()
         for i, (a, b) in enumerate(zip(layer.bits(), ref)):
             assert np.array_equal(a, b), "replay %d, output %d" % (replay, i)
+
+
+def test_two_layers_on_two_streams_at_once():
+    """The library keeps no mutable state between calls: two different
+    layers launched on two side streams at the same time each give the bits
+    they give alone."""
+    a, b = Layer(seed=81), Layer(seed=91)
+    refs = []
+    for layer in (a, b):
+        layer.clear()
+        layer.run()
+        torch.cuda.synchronize()
+        refs.append(layer.bits())
+        layer.clear()
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()   # default priority
+    for _ in range(2):                                   # interleave the launches of both
+        a.run(stream=s1.cuda_stream)
+        b.run(stream=s2.cuda_stream)
+    torch.cuda.synchronize()
+    for layer, ref in ((a, refs[0]), (b, refs[1])):
+        for x, y in zip(layer.bits(), ref):
+            assert np.array_equal(x, y)
