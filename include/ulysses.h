@@ -153,9 +153,17 @@ size_t attn_fwd_workspace_bytes(int64_t N, int32_t hq, int32_t hkv, int32_t d);
 
 /*
  * attn_fwd over packed documents: key j is visible to query i iff both lie in
- * the same document [cu[b], cu[b+1]) and (causal == 0 or j <= i).
+ * the same document [cu[b], cu[b+1]) and (causal == 0 or j <= i). Several
+ * samples packed into one sequence must not attend across their boundaries
+ * ("Ulysses sequence parallelism", Configure, on sp_attn_implementation:
+ * packed samples need an attention that respects sample boundaries;
+ * "Ulysses Sequence Parallelism for Million-Token Context Training",
+ * Ecosystem Integration, TRL SFTTrainer: packing several samples into one
+ * sequence).
  * cu_seqlens: DEVICE int32 [n_seqs + 1], checked by ulysses_check_cu_seqlens
- * on its host copy (the kernels trust it). max_seqlen: longest document,
+ * on its host copy (the kernels trust it; a table that fails the check
+ * gives wrong values, but every range the kernels derive from it is cut to
+ * [0, N), so no access leaves the tensors). max_seqlen: longest document,
  * used only for validation (must be in [1, N]).
  */
 int attn_fwd_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *o,
@@ -179,7 +187,15 @@ size_t attn_bwd_workspace_bytes(int64_t N, int32_t hq, int32_t hkv, int32_t d, i
 
 /*
  * Attention backward: gradients of L = sum(dout * o) for the attn_fwd call
- * with the same arguments. o and lse are that call's outputs.
+ * with the same arguments, i.e. the backward pass of the local attention of
+ * "How Ulysses Sequence Parallelism Works", step 4, which training through
+ * it needs (Ecosystem Integration, Transformers Trainer: the gradients must
+ * come out correct). The scores are recomputed tile by tile from the saved
+ * lse instead of being stored ("The Challenge of Long Sequence Training":
+ * tiled attention keeps O(n) memory for O(n^2) work):
+ *   D_i = dout_i . o_i,  p_ij = exp(s_ij - lse_i),  ds_ij = p_ij (dout_i . v_j - D_i),
+ *   dq_i = scale sum_j ds_ij k_j,  dk_j = scale sum_i ds_ij q_i,  dv_j = sum_i p_ij dout_i.
+ * o and lse are that call's outputs.
  * dq [N] x hq x d, dk, dv [N] x hkv x d with their own token strides; they
  * are overwritten (not accumulated). dk and dv sum over the query heads of
  * each GQA group. dq, dk and dv may be views into one fused
@@ -196,7 +212,10 @@ int attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint
              int64_t dk_stride, int64_t dv_stride, float scale, int32_t causal, void *ws,
              size_t ws_bytes, hipStream_t stream);
 
-/* attn_bwd over packed documents (mask as in attn_fwd_varlen). */
+/* attn_bwd over packed documents: the gradients of attn_fwd_varlen with the
+ * same arguments (mask, cu_seqlens and max_seqlen as there: "Ulysses
+ * sequence parallelism", Configure, packed samples must not attend across
+ * their boundaries). */
 int attn_bwd_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *o,
                     const float *lse, const uint16_t *dout, uint16_t *dq, uint16_t *dk,
                     uint16_t *dv, int64_t N, int32_t hq, int32_t hkv, int32_t d,
@@ -208,12 +227,20 @@ int attn_bwd_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
 /*
  * The two steps of attn_bwd as separate calls, for callers that schedule them
  * on their own (e.g. to overlap the second with other work). attn_bwd is
- * exactly attn_bwd_dq followed by attn_bwd_dkdv on the same stream.
+ * exactly attn_bwd_dq followed by attn_bwd_dkdv on the same stream. The
+ * split follows the gradient's definition (attn_bwd above; "The Challenge of
+ * Long Sequence Training"): dq sums over keys, dk and dv over queries, so
+ * each step is one pass that recomputes the scores it needs.
  *
  * attn_bwd_dq: fills ws (D, LSE*log2(e), the transposed copies of K, Q and
  *   dO) and writes dq.
- * attn_bwd_dkdv: dk and dv, reading ws as left by attn_bwd_dq with the same
- *   arguments (ws must not be modified in between).
+ * attn_bwd_dkdv: dk and dv. It reads D, LSE*log2(e) and the transposed
+ *   copies of Q and dO from ws as left by attn_bwd_dq with the same
+ *   arguments (not to be modified in between), and writes two other regions
+ *   of ws: the order of its key blocks (packed documents) and its float32
+ *   partial dK/dV (when it splits its query ranges, see
+ *   attn_bwd_workspace_bytes). Calls that may run at the same time therefore
+ *   need workspaces of their own.
  * cu_seqlens: device table as in attn_fwd_varlen, or NULL for one document
  * (n_seqs is then ignored). Errors as attn_bwd.
  */
@@ -228,7 +255,7 @@ int attn_bwd_dkdv(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
                   const uint16_t *dout, uint16_t *dk, uint16_t *dv, int64_t N, int32_t hq,
                   int32_t hkv, int32_t d, int64_t q_stride, int64_t k_stride, int64_t v_stride,
                   int64_t do_stride, int64_t dk_stride, int64_t dv_stride, float scale,
-                  int32_t causal, const int32_t *cu_seqlens, int32_t n_seqs, const void *ws,
+                  int32_t causal, const int32_t *cu_seqlens, int32_t n_seqs, void *ws,
                   size_t ws_bytes, hipStream_t stream);
 
 /*

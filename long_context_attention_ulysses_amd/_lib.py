@@ -7,6 +7,7 @@ is not built this module raises ImportError: there is no fallback path.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional, Sequence
@@ -98,9 +99,10 @@ def _check(rc: int, where: str):
 
 
 def _stream(stream, device) -> int:
-    """The given stream, else torch's current stream on the tensors' device."""
+    """The given stream (a raw HIP stream handle or a torch stream), else
+    torch's current stream on the tensors' device."""
     if stream is not None:
-        return int(stream)
+        return int(getattr(stream, "cuda_stream", stream))
     return torch.cuda.current_stream(device).cuda_stream
 
 
@@ -235,9 +237,23 @@ def attn_fwd_workspace_bytes(N: int, hq: int, hkv: int, d: int) -> int:
     return int(_L.attn_fwd_workspace_bytes(N, hq, hkv, d))
 
 
-def _workspace(nbytes: int, like):
-    """Device memory for a workspace (torch's allocator; 256-byte aligned)."""
-    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=like.device)
+def _allocation_stream(handle: int, device):
+    """Context under which torch's caching allocator hands out memory for
+    work on stream `handle`: that stream itself. A block taken on another
+    stream and freed when the call returns could go to that stream's next
+    allocation while the kernels launched here still use it; a block taken
+    on the stream the kernels run on is only reused by later work on the
+    same stream, which runs after them."""
+    if handle == torch.cuda.current_stream(device).cuda_stream:
+        return contextlib.nullcontext()
+    return torch.cuda.stream(torch.cuda.ExternalStream(handle, device=device))
+
+
+def _workspace(nbytes: int, like, stream_handle: int):
+    """Device memory for a workspace (torch's allocator; 256-byte aligned),
+    allocated on the stream the call launches on."""
+    with _allocation_stream(stream_handle, like.device):
+        return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=like.device)
 
 
 def _qkv_dims(q, k):
@@ -259,16 +275,17 @@ def attn_fwd(q, k, v, o, lse, scale: float, causal: bool = True, cu_seqlens=None
                a.rows(o, "o", N, hq, d))
     a(lse, "lse", kind=torch.float32, shape=(hq, N), contiguous=True)
     n_seqs = a.cu(cu_seqlens, N) if cu_seqlens is not None else 0
+    sh = a.stream(stream)
     if ws is None:
-        ws = _workspace(attn_fwd_workspace_bytes(N, hq, hkv, d), q)
+        ws = _workspace(attn_fwd_workspace_bytes(N, hq, hkv, d), q, sh)
     wsb = a.ws(ws)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), N, hq, hkv, d) + strides + (float(scale),
                                                                                         int(bool(causal)))
     if cu_seqlens is None:
-        _check(_L.attn_fwd(*args, _ptr(ws), wsb, a.stream(stream)), "attn_fwd")
+        _check(_L.attn_fwd(*args, _ptr(ws), wsb, sh), "attn_fwd")
     else:
-        _check(_L.attn_fwd_varlen(*args, _ptr(cu_seqlens), n_seqs, int(max_seqlen or N), _ptr(ws), wsb,
-                                  a.stream(stream)), "attn_fwd_varlen")
+        _check(_L.attn_fwd_varlen(*args, _ptr(cu_seqlens), n_seqs, int(max_seqlen or N), _ptr(ws), wsb, sh),
+               "attn_fwd_varlen")
 
 
 def attn_bwd_workspace_bytes(N: int, hq: int, hkv: int, d: int, n_seqs: int = 1) -> int:
@@ -293,16 +310,17 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, scale: float, causal: bool = Tru
     st, st_o, st_do = _bwd_args(a, q, k, v, o, lse, dout, N, hq, hkv, d)
     st_g = (a.rows(dq, "dq", N, hq, d), a.rows(dk, "dk", N, hkv, d), a.rows(dv, "dv", N, hkv, d))
     n_seqs = a.cu(cu_seqlens, N) if cu_seqlens is not None else 1
+    sh = a.stream(stream)
     if ws is None:
-        ws = _workspace(attn_bwd_workspace_bytes(N, hq, hkv, d, n_seqs), q)
+        ws = _workspace(attn_bwd_workspace_bytes(N, hq, hkv, d, n_seqs), q, sh)
     ws_bytes = a.ws(ws)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
             N, hq, hkv, d) + st + (st_o, st_do) + st_g + (float(scale), int(bool(causal)))
     if cu_seqlens is None:
-        _check(_L.attn_bwd(*args, _ptr(ws), ws_bytes, a.stream(stream)), "attn_bwd")
+        _check(_L.attn_bwd(*args, _ptr(ws), ws_bytes, sh), "attn_bwd")
     else:
-        _check(_L.attn_bwd_varlen(*args, _ptr(cu_seqlens), n_seqs, int(max_seqlen or N), _ptr(ws), ws_bytes,
-                                  a.stream(stream)), "attn_bwd_varlen")
+        _check(_L.attn_bwd_varlen(*args, _ptr(cu_seqlens), n_seqs, int(max_seqlen or N), _ptr(ws), ws_bytes, sh),
+               "attn_bwd_varlen")
 
 
 def attn_bwd_dq(q, k, v, o, lse, dout, dq, scale: float, causal: bool = True, ws=None, cu_seqlens=None,
@@ -321,7 +339,9 @@ def attn_bwd_dq(q, k, v, o, lse, dout, dq, scale: float, causal: bool = True, ws
 
 def attn_bwd_dkdv(q, k, v, lse, dout, dk, dv, scale: float, causal: bool = True, ws=None, cu_seqlens=None,
                   stream=None) -> None:
-    """Second step of attn_bwd: dk and dv, reading D from ws (left by attn_bwd_dq)."""
+    """Second step of attn_bwd: dk and dv, reading D, LSE and the transposed
+    copies from ws (left there by attn_bwd_dq) and overwriting ws's key-block
+    order and dK/dV partial regions (so concurrent calls need their own ws)."""
     a = _Args("attn_bwd_dkdv")
     N, hq, hkv, d = _qkv_dims(q, k)
     st, _, st_do = _bwd_args(a, q, k, v, None, lse, dout, N, hq, hkv, d)
@@ -445,11 +465,12 @@ def tiled_mlp_fwd(x, w_gu, w_down, y, tile: int, ws=None, stream=None) -> None:
     I = w_down.shape[1]
     for t, nm, sh in ((x, "x", (n, H)), (w_gu, "w_gu", (2 * I, H)), (w_down, "w_down", (H, I)), (y, "y", (n, H))):
         a(t, nm, shape=sh, contiguous=True)
+    sh = a.stream(stream)
     if ws is None:
-        ws = _workspace(tiled_mlp_workspace_bytes(tile, H, I), x)
+        ws = _workspace(tiled_mlp_workspace_bytes(tile, H, I), x, sh)
     wsb = a.ws(ws)
-    _check(_L.tiled_mlp_fwd(_ptr(x), _ptr(w_gu), _ptr(w_down), _ptr(y), n, H, I, tile, _ptr(ws), wsb,
-                            a.stream(stream)), "tiled_mlp_fwd")
+    _check(_L.tiled_mlp_fwd(_ptr(x), _ptr(w_gu), _ptr(w_down), _ptr(y), n, H, I, tile, _ptr(ws), wsb, sh),
+           "tiled_mlp_fwd")
 
 
 def tiled_mlp_bwd(x, w_gu, w_down, dy, dx, dw_gu, dw_down, tile: int, accumulate: bool = False, ws=None,
@@ -466,8 +487,9 @@ def tiled_mlp_bwd(x, w_gu, w_down, dy, dx, dw_gu, dw_down, tile: int, accumulate
         a(t, nm, shape=sh, contiguous=True)
     a(dw_gu, "dw_gu", kind=torch.float32, shape=(2 * I, H), contiguous=True)
     a(dw_down, "dw_down", kind=torch.float32, shape=(H, I), contiguous=True)
+    sh = a.stream(stream)
     if ws is None:
-        ws = _workspace(tiled_mlp_workspace_bytes(tile, H, I), x)
+        ws = _workspace(tiled_mlp_workspace_bytes(tile, H, I), x, sh)
     wsb = a.ws(ws)
     _check(_L.tiled_mlp_bwd(_ptr(x), _ptr(w_gu), _ptr(w_down), _ptr(dy), _ptr(dx), _ptr(dw_gu), _ptr(dw_down), n,
-                            H, I, tile, int(bool(accumulate)), _ptr(ws), wsb, a.stream(stream)), "tiled_mlp_bwd")
+                            H, I, tile, int(bool(accumulate)), _ptr(ws), wsb, sh), "tiled_mlp_bwd")

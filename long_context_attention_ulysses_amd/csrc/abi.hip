@@ -137,7 +137,7 @@ int attn_bwd_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
                   uint16_t *dv, int64_t N, int32_t hq, int32_t hkv, int32_t d, int64_t qs,
                   int64_t ks, int64_t vs, int64_t os, int64_t dos, int64_t dqs, int64_t dks,
                   int64_t dvs, float scale, int32_t causal, const int32_t *cu, int32_t n_seqs,
-                  const void *ws, size_t ws_bytes, int parts, hipStream_t stream) {
+                  void *ws, size_t ws_bytes, int parts, hipStream_t stream) {
   int rc = check_attn_common(q, k, v, N, hq, hkv, d, qs, ks, vs, scale);
   if (rc) return rc;
   const bool want_dq = parts & 1, want_dkv = parts & 2;
@@ -200,7 +200,7 @@ int attn_bwd_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
   p.dq_stride = dqs;
   p.dk_stride = dks;
   p.dv_stride = dvs;
-  p.ws = static_cast<char *>(const_cast<void *>(ws));
+  p.ws = static_cast<char *>(ws);
   return launch_attn_bwd(s, p, parts, stream);
 }
 
@@ -334,7 +334,7 @@ int attn_bwd_dkdv(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
                   const uint16_t *dout, uint16_t *dk, uint16_t *dv, int64_t N, int32_t hq,
                   int32_t hkv, int32_t d, int64_t q_stride, int64_t k_stride, int64_t v_stride,
                   int64_t do_stride, int64_t dk_stride, int64_t dv_stride, float scale,
-                  int32_t causal, const int32_t *cu_seqlens, int32_t n_seqs, const void *ws,
+                  int32_t causal, const int32_t *cu_seqlens, int32_t n_seqs, void *ws,
                   size_t ws_bytes, hipStream_t stream) {
   if (cu_seqlens && (n_seqs <= 0 || n_seqs > N)) return ULY_E_SHAPE;
   return attn_bwd_impl(q, k, v, nullptr, lse, dout, nullptr, dk, dv, N, hq, hkv, d, q_stride,

@@ -202,7 +202,7 @@ __device__ __forceinline__ void pipeline_reads_mfma() {
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
 // Document containing token t: largest b with cu[b] <= t (cu strictly increasing).
-__device__ __forceinline__ int doc_of(const int32_t *cu, int n_seqs, int64_t t) {
+__host__ __device__ __forceinline__ int doc_of(const int32_t *cu, int n_seqs, int64_t t) {
   int lo = 0, hi = n_seqs - 1;
   while (lo < hi) {
     int mid = (lo + hi + 1) >> 1;
@@ -217,8 +217,20 @@ struct KeyRange {
   int64_t lo, hi;
 };
 
-__device__ __forceinline__ KeyRange key_range(const int32_t *cu, int n_seqs, int64_t N, int causal,
-                                              int64_t i) {
+// A range cut to [0, N) with lo <= hi. For a valid cu_seqlens table this
+// changes nothing; for a table the host did not check (entries past N,
+// negative or unsorted) it keeps every tile index the kernels derive from
+// the range inside the tensors, so such a table gives wrong values rather
+// than out-of-range addresses.
+__host__ __device__ __forceinline__ KeyRange clamp_range(KeyRange r, int64_t N) {
+  if (r.hi > N) r.hi = N;
+  if (r.lo < 0) r.lo = 0;
+  if (r.lo > r.hi) r.lo = r.hi;
+  return r;
+}
+
+__host__ __device__ __forceinline__ KeyRange key_range(const int32_t *cu, int n_seqs, int64_t N, int causal,
+                                                       int64_t i) {
   KeyRange r;
   if (cu) {
     int b = doc_of(cu, n_seqs, i);
@@ -229,12 +241,12 @@ __device__ __forceinline__ KeyRange key_range(const int32_t *cu, int n_seqs, int
     r.hi = N;
   }
   if (causal) r.hi = i + 1;
-  return r;
+  return clamp_range(r, N);
 }
 
 // Queries that see key j: [lo, hi).
-__device__ __forceinline__ KeyRange query_range(const int32_t *cu, int n_seqs, int64_t N,
-                                                int causal, int64_t j) {
+__host__ __device__ __forceinline__ KeyRange query_range(const int32_t *cu, int n_seqs, int64_t N,
+                                                         int causal, int64_t j) {
   KeyRange r;
   if (cu) {
     int b = doc_of(cu, n_seqs, j);
@@ -245,7 +257,7 @@ __device__ __forceinline__ KeyRange query_range(const int32_t *cu, int n_seqs, i
     r.hi = N;
   }
   if (causal) r.lo = j;
-  return r;
+  return clamp_range(r, N);
 }
 
 }  // namespace uly

@@ -1,0 +1,54 @@
+// Host build of the attention kernels' key/query range helpers: every range
+// they return lies in [0, N) with lo <= hi, for valid and invalid
+// cu_seqlens tables alike; for valid tables it is the document's range.
+#include <stdio.h>
+
+#include "attn_common.h"
+
+using uly::KeyRange;
+
+static int check(const int32_t *cu, int n_seqs, int64_t N, bool valid) {
+  int bad = 0;
+  for (int causal = 0; causal < 2; ++causal)
+    for (int64_t t = 0; t < N; ++t) {
+      const KeyRange k = uly::key_range(cu, n_seqs, N, causal, t);
+      const KeyRange q = uly::query_range(cu, n_seqs, N, causal, t);
+      for (const KeyRange &r : {k, q})
+        if (r.lo < 0 || r.hi > N || r.lo > r.hi) {
+          printf("out of range: t=%lld causal=%d [%lld, %lld)\n", (long long)t, causal, (long long)r.lo,
+                 (long long)r.hi);
+          ++bad;
+        }
+      if (valid) {
+        int b = 0;
+        while (cu[b + 1] <= t) ++b;
+        const int64_t lo = cu[b], hi = cu[b + 1];
+        if (k.lo != lo || k.hi != (causal ? t + 1 : hi) || q.lo != (causal ? t : lo) || q.hi != hi) {
+          printf("wrong range: t=%lld causal=%d\n", (long long)t, causal);
+          ++bad;
+        }
+      }
+    }
+  return bad;
+}
+
+int main() {
+  const int32_t good[] = {0, 3, 4, 10, 16};
+  const int32_t past_end[] = {0, 5, 40};          // last document ends past N = 16
+  const int32_t negative[] = {-7, 2, 16};
+  const int32_t unsorted[] = {0, 12, 5, 16};
+  const int32_t huge[] = {0, 2147483647};
+  int bad = check(good, 4, 16, true);
+  bad += check(past_end, 2, 16, false);
+  bad += check(negative, 2, 16, false);
+  bad += check(unsorted, 3, 16, false);
+  bad += check(huge, 1, 16, false);
+  bad += check(nullptr, 0, 16, false);
+  // with no table the ranges are the dense ones
+  for (int64_t t = 0; t < 16; ++t) {
+    const KeyRange k = uly::key_range(nullptr, 0, 16, 1, t), q = uly::query_range(nullptr, 0, 16, 1, t);
+    if (k.lo != 0 || k.hi != t + 1 || q.lo != t || q.hi != 16) ++bad;
+  }
+  printf("%s\n", bad ? "FAIL" : "OK");
+  return bad ? 1 : 0;
+}

@@ -172,3 +172,38 @@ def test_binding_rejects_host_tensors():
         uly.attn_fwd(q, k, k, q.clone(), lse, 0.125, ws=ws)
     with pytest.raises(TypeError):
         uly.ring_grad_sum([q.numpy()], q)
+
+
+def test_workspace_is_allocated_on_the_launch_stream(monkeypatch):
+    """When the binding allocates a workspace itself (ws=None), it takes the
+    memory on the stream the kernels are launched on, so torch's caching
+    allocator cannot hand that block to other work before the kernels are
+    done. Checked with stand-ins for torch's stream objects (no GPU)."""
+    import contextlib
+
+    import long_context_attention_ulysses_amd._lib as lib
+
+    active, made = [], []
+
+    class FakeStream:
+        def __init__(self, handle, device=None):
+            self.cuda_stream = handle
+
+    @contextlib.contextmanager
+    def enter(s):
+        active.append(s.cuda_stream)
+        yield
+        active.pop()
+
+    class Like:
+        device = "cuda:0"
+
+    monkeypatch.setattr(lib.torch.cuda, "current_stream", lambda device=None: FakeStream(5))
+    monkeypatch.setattr(lib.torch.cuda, "ExternalStream", FakeStream)
+    monkeypatch.setattr(lib.torch.cuda, "stream", enter)
+    monkeypatch.setattr(lib.torch, "empty", lambda *a, **k: made.append(active[-1] if active else "current"))
+    lib._workspace(100, Like(), 9)      # a side stream: allocate under it
+    lib._workspace(100, Like(), 5)      # torch's current stream: no switch
+    assert made == [9, "current"]
+    assert lib._stream(FakeStream(11), "cuda:0") == 11 and lib._stream(12, "cuda:0") == 12
+    assert lib._stream(None, "cuda:0") == 5

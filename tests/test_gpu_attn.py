@@ -9,12 +9,18 @@ import torch
 
 import oracle
 import workloads
+from tests import uniform_scores
 from tests._gpu import (FWD_MAX_ABS, FWD_REL, GRAD_MAX_ABS, GRAD_REL, LSE_MAX_ABS, assert_close, dev,
                         f64, host, sentinel)
 
 pytestmark = pytest.mark.gpu
 
 uly = pytest.importorskip("long_context_attention_ulysses_amd")
+
+
+# Keys at the end of the sequence whose dK/dV the sampled tests compare with
+# the oracle (only the query rows in that tail see them).
+TAIL_KEYS = 512
 
 
 class Run:
@@ -171,7 +177,8 @@ def _sample_rows(N, n_local, count, seed):
 def test_workload_head_shard_sampled(name):
     """Rank 0's head shard at the workload's full size, in the launch shape the
     benchmark times; oracle on sampled query rows (O, LSE, dQ), on the last
-    128 keys (dK, dV) and, where the oracle is fast enough, on the first 128."""
+    512 keys (dK, dV) and, where the oracle is fast enough, on the first 128;
+    the Q = 0 / K = 0 closed forms check every key at 64K and 256K."""
     w = workloads.WORKLOADS[name]
     print("workload %s N=%d hq=%d hkv=%d" % (name, w.N, w.hq, w.hkv), flush=True)
     qkv = workloads.gen_head_shard(w, 0)
@@ -187,7 +194,7 @@ def test_workload_head_shard_sampled(name):
     o_ref, lse_ref = oracle.attn_fwd(q, k, v, w.scale, True, cu, rows=rows)
     assert_close(name + " O[rows]", oracle.bf16_to_f64(o[rows]), o_ref, FWD_MAX_ABS, FWD_REL)
     assert_close(name + " LSE[rows]", lse[:, rows].astype(np.float64), lse_ref, LSE_MAX_ABS, 1.0)
-    klo = w.N - 128
+    klo = w.N - TAIL_KEYS
     dq_ref, dk_ref, dv_ref = oracle.attn_bwd(q, k, v, dy, w.scale, True, cu, rows=rows, key_lo=klo)
     assert_close(name + " dQ[rows]", oracle.bf16_to_f64(dq[rows]), dq_ref, GRAD_MAX_ABS, GRAD_REL)
     assert_close(name + " dK[tail]", oracle.bf16_to_f64(dk[klo:]), dk_ref, GRAD_MAX_ABS, GRAD_REL)
@@ -232,7 +239,7 @@ def test_unsplit_grids_sampled(N, hq, hkv, d):
     """Problems large enough that no kernel splits its ranges (at least 512
     blocks per grid), for the head-group sizes and head dim the workloads
     above do not reach unsplit; oracle on sampled query rows and the last
-    128 keys."""
+    512 keys."""
     print("unsplit N=%d hq=%d hkv=%d d=%d" % (N, hq, hkv, d), flush=True)
     qkv = workloads.normal_bf16((N, hq + 2 * hkv, d), seed=N + hq * 7 + d, sigma=0.5)
     dy = workloads.normal_bf16((N, hq, d), seed=N + hq * 11 + d)
@@ -245,7 +252,7 @@ def test_unsplit_grids_sampled(N, hq, hkv, d):
     o_ref, lse_ref = oracle.attn_fwd(q, k, v, scale, True, None, rows=rows)
     assert_close("O[rows]", oracle.bf16_to_f64(o[rows]), o_ref, FWD_MAX_ABS, FWD_REL)
     assert_close("LSE[rows]", lse[:, rows].astype(np.float64), lse_ref, LSE_MAX_ABS, 1.0)
-    klo = N - 128
+    klo = N - TAIL_KEYS
     dq_ref, dk_ref, dv_ref = oracle.attn_bwd(q, k, v, dy, scale, True, None, rows=rows, key_lo=klo)
     assert_close("dQ[rows]", oracle.bf16_to_f64(dq[rows]), dq_ref, GRAD_MAX_ABS, GRAD_REL)
     assert_close("dK[tail]", oracle.bf16_to_f64(dk[klo:]), dk_ref, GRAD_MAX_ABS, GRAD_REL)
@@ -316,24 +323,40 @@ def test_separate_and_strided_layouts_give_identical_bits():
         assert np.array_equal(a, b)
 
 
-def test_q_zero_closed_form_full_size():
-    """Q = 0 at 64K: o_i = mean(v_0..v_i), LSE_i = ln(i+1) for every row, and
-    dK = 0 exactly (checked over all N rows via prefix sums)."""
-    w = workloads.WORKLOADS["64k"]
+@pytest.mark.parametrize("name", ["64k", "256k"])
+@pytest.mark.parametrize("zero", ["q", "k"])
+def test_uniform_scores_closed_form_full_size(name, zero):
+    """Q = 0 or K = 0 at the full 64K and 256K head shards, in the launch
+    shape the benchmark times: every visible score is zero, so attention and
+    all its gradients have closed forms in prefix and suffix sums
+    (tests/uniform_scores.py). Every row of O, LSE and dV is compared, every
+    row of dQ (Q = 0) or dK (K = 0), and the other of the two must be
+    exactly zero. dV and dK cover every key block's whole walk through the
+    dK/dV kernel (4096 tiles for the first block at 64K, 16384 at 256K)."""
+    w = workloads.WORKLOADS[name]
+    print("uniform scores %s N=%d hq=%d hkv=%d, %s = 0" % (name, w.N, w.hq, w.hkv, zero), flush=True)
     qkv = workloads.gen_head_shard(w, 0)
-    qkv[:, :w.hq] = 0
+    if zero == "q":
+        qkv[:, :w.hq] = 0
+    else:
+        qkv[:, w.hq:w.hq + w.hkv] = 0
     dy = workloads.gen_dy_head_shard(w, 0)
     r = Run(qkv, w.hq, w.hkv, w.scale, True)
     o, lse = r.fwd()
-    v = oracle.bf16_to_f64(qkv[:, w.hq + w.hkv:])
-    mean = np.cumsum(v, axis=0) / np.arange(1, w.N + 1)[:, None, None]
-    G = w.hq // w.hkv
-    for h in range(w.hq):
-        assert_close("Q=0 O head %d" % h, oracle.bf16_to_f64(o[:, h]), mean[:, h // G], FWD_MAX_ABS, FWD_REL)
-    assert_close("Q=0 LSE", lse.astype(np.float64), np.broadcast_to(np.log(np.arange(1, w.N + 1)), lse.shape),
-                 LSE_MAX_ABS, 1.0)
     dq, dk, dv = r.bwd(dy)
-    assert np.all(oracle.bf16_to_f64(dk) == 0.0)
+    q, k, v = (oracle.bf16_to_f64(x) for x in _split(qkv, w.hq, w.hkv))
+    o_ref, lse_ref, dq_ref, dk_ref, dv_ref = uniform_scores.uniform_causal(
+        q, k, v, oracle.bf16_to_f64(dy), w.scale, want_dq=zero == "q", want_dk=zero == "k")
+    tag = "%s %s=0 " % (name, zero.upper())
+    assert_close(tag + "O", oracle.bf16_to_f64(o), o_ref, FWD_MAX_ABS, FWD_REL)
+    assert_close(tag + "LSE", lse.astype(np.float64), lse_ref, LSE_MAX_ABS, 1.0)
+    assert_close(tag + "dV", oracle.bf16_to_f64(dv), dv_ref, GRAD_MAX_ABS, GRAD_REL)
+    if zero == "q":
+        assert_close(tag + "dQ", oracle.bf16_to_f64(dq), dq_ref, GRAD_MAX_ABS, GRAD_REL)
+        assert np.all(oracle.bf16_to_f64(dk) == 0.0), "dK must be exactly 0 when Q = 0"
+    else:
+        assert_close(tag + "dK", oracle.bf16_to_f64(dk), dk_ref, GRAD_MAX_ABS, GRAD_REL)
+        assert np.all(oracle.bf16_to_f64(dq) == 0.0), "dQ must be exactly 0 when K = 0"
 
 
 def test_determinism_and_causality():

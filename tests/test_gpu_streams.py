@@ -77,6 +77,38 @@ def test_side_stream_gives_default_stream_bits():
         assert np.array_equal(a, b)
 
 
+def test_side_stream_with_binding_allocated_workspaces():
+    """ws=None on a side stream: the binding allocates the workspaces on that
+    stream, so memory the default stream allocates and overwrites right
+    after each call cannot be the workspace the side stream's kernels are
+    still using."""
+    layer = Layer(seed=75)
+    layer.clear()
+    layer.run()
+    torch.cuda.synchronize()
+    ref = layer.bits()
+    layer.clear()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()                 # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    s = layer.shard
+    q, k, v = s[:, :hq], s[:, hq:hq + hkv], s[:, hq + hkv:]
+    g = layer.dqkv
+    junk = []
+    uly.ulysses_seq_to_head(layer.x, layer.send, P, SEGS, stream=side.cuda_stream)
+    uly.attn_fwd(q, k, v, layer.o, layer.lse, SCALE, True, stream=side.cuda_stream)
+    junk.append(torch.full((layer.wsf.numel(),), 0x7F, dtype=torch.uint8, device="cuda"))
+    uly.attn_bwd(q, k, v, layer.o, layer.lse, layer.dy, g[:, :hq], g[:, hq:hq + hkv], g[:, hq + hkv:], SCALE,
+                 True, stream=side.cuda_stream)
+    junk.append(torch.full((layer.wsb.numel(),), 0x7F, dtype=torch.uint8, device="cuda"))
+    uly.ulysses_head_to_seq(layer.o.view(P, n, hq, d), layer.o_seq, P, [Hq], stream=side.cuda_stream)
+    uly.ulysses_head_to_seq(layer.dqkv.view(P, n, ht, d), layer.g_seq, P, SEGS, stream=side.cuda_stream)
+    side.synchronize()
+    torch.cuda.synchronize()
+    for a, b in zip(layer.bits(), ref):
+        assert np.array_equal(a, b)
+
+
 def test_layer_captured_in_a_hip_graph_replays_exactly():
     layer = Layer()
     layer.clear()

@@ -44,15 +44,25 @@ def test_finite_differences():
 
 
 def test_closed_forms():
-    x, w_gu, w_down, dy = _case(n=3, H=8, I=8)
-    I = 8
-    zero_gate = w_gu.copy()
-    zero_gate[:I] = 0.0                       # silu(0) = 0: no output
-    assert np.all(oracle.swiglu_mlp(x, zero_gate, w_down) == 0)
-    # with the gate at 0, d silu/dg = 1/2: dx = (1/2) (dy Wd * up) Wg
-    dx, _, _ = oracle.swiglu_mlp_bwd(x, zero_gate, w_down, dy)
+    """A gate that is zero for every token while W_gate is not: x lives in
+    the first half of the hidden dims and the gate rows in the second half,
+    so gate = x W_gate^T = 0. Then silu(0) = 0 and d silu/dg = 1/2 give
+      y = 0,  dx = (1/2) ((dy W_down) * up) W_gate,
+      dW_gate = ((1/2) (dy W_down) * up)^T x,  dW_up = 0,  dW_down = 0,
+    with up = x W_up^T; dx and dW_gate are not zero."""
+    n, H, I = 5, 8, 6
+    x, w_gu, w_down, dy = _case(n=n, H=H, I=I, seed=5)
+    x[:, H // 2:] = 0.0
+    w_gu[:I, :H // 2] = 0.0
+    assert np.all(x @ w_gu[:I].T == 0.0) and np.any(w_gu[:I] != 0.0)
+    assert np.all(oracle.swiglu_mlp(x, w_gu, w_down) == 0.0)
+    dx, dwg, dwd = oracle.swiglu_mlp_bwd(x, w_gu, w_down, dy)
     up = x @ w_gu[I:].T
-    np.testing.assert_allclose(dx, 0.5 * ((dy @ w_down) * up) @ zero_gate[:I], atol=1e-12)
+    dgate = 0.5 * (dy @ w_down) * up
+    np.testing.assert_allclose(dx, dgate @ w_gu[:I], atol=1e-12)
+    np.testing.assert_allclose(dwg[:I], dgate.T @ x, atol=1e-12)
+    assert np.all(dwg[I:] == 0.0) and np.all(dwd == 0.0)
+    assert np.max(np.abs(dx)) > 1e-3 and np.max(np.abs(dwg[:I])) > 1e-3
 
 
 def test_token_tiles_are_independent():
