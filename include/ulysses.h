@@ -55,6 +55,10 @@ extern "C" {
 #define ULY_E_HIP (-9)       /* a HIP launch failed; see uly_last_error() */
 #define ULY_E_SEQLENS (-10)  /* cu_seqlens is not 0 = c0 < c1 < ... < c_n = N */
 #define ULY_E_ALIGN (-11)    /* pointer not 16-byte aligned or stride not a multiple of 8 */
+#define ULY_E_SCRATCH (-12)  /* attn_fwd_noalloc: problem needs more than its static scratch */
+
+/* Bytes of the static per-GPU scratch buffer attn_fwd_noalloc works in. */
+#define ULY_NOALLOC_SCRATCH_BYTES (80u << 20)
 
 /* Text for a status code. Never NULL. */
 const char *uly_status_string(int status);
@@ -142,6 +146,28 @@ int attn_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *
              int64_t N, int32_t hq, int32_t hkv, int32_t d, int64_t q_stride, int64_t k_stride,
              int64_t v_stride, int64_t o_stride, float scale, int32_t causal, void *ws,
              size_t ws_bytes, hipStream_t stream);
+
+/*
+ * attn_fwd without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops that must not allocate, harnesses that forbid it). Same
+ * arguments, result bits and errors as attn_fwd, except that the workspace
+ * is a static buffer of ULY_NOALLOC_SCRATCH_BYTES (80 MiB) that the library
+ * holds on every GPU it runs on until the process ends. Problems whose
+ * attn_fwd_workspace_bytes(N, hq, hkv, d) exceed that return ULY_E_SCRATCH
+ * (before anything is launched). At d = 128 that allows up to 327,680
+ * tokens with one KV head or 163,840 with two; every head shard of the
+ * 8K, 64K, packed 64K and 256K workloads fits.
+ * The device is the stream's (the current device for stream 0). The first
+ * call on a device looks up the buffer's address there; that lookup can
+ * fail with ULY_E_HIP. Every call on a GPU shares that GPU's buffer and
+ * leaves its contents behind: calls that may overlap on one GPU (different
+ * streams, or threads) race on it and must be serialised by the caller.
+ */
+int attn_fwd_noalloc(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *o,
+                     float *lse, int64_t N, int32_t hq, int32_t hkv, int32_t d, int64_t q_stride,
+                     int64_t k_stride, int64_t v_stride, int64_t o_stride, float scale,
+                     int32_t causal, hipStream_t stream);
 
 /* Workspace attn_fwd and attn_fwd_varlen need: hkv * d * roundup(N, 64) * 2
  * bytes (the transposed V), rounded up to 256, and, when there are fewer than

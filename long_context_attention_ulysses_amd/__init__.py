@@ -14,12 +14,14 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     STATUS,
     CODE,
+    NOALLOC_SCRATCH_BYTES,
     UlyssesError,
     attn_bwd,
     attn_bwd_dkdv,
     attn_bwd_dq,
     attn_bwd_workspace_bytes,
     attn_fwd,
+    attn_fwd_noalloc,
     attn_fwd_workspace_bytes,
     attn_lse_merge,
     raw,

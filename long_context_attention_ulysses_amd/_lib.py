@@ -19,7 +19,7 @@ ULY_OK = 0
 STATUS = {
     -1: "ULY_E_NULL", -2: "ULY_E_SHAPE", -3: "ULY_E_DIV_P", -4: "ULY_E_GQA", -5: "ULY_E_HEADDIM",
     -6: "ULY_E_STRIDE", -7: "ULY_E_WORKSPACE", -8: "ULY_E_ALIAS", -9: "ULY_E_HIP",
-    -10: "ULY_E_SEQLENS", -11: "ULY_E_ALIGN",
+    -10: "ULY_E_SEQLENS", -11: "ULY_E_ALIGN", -12: "ULY_E_SCRATCH",
 }
 CODE = {v: k for k, v in STATUS.items()}
 
@@ -51,6 +51,8 @@ _SIGS = {
                   _p], ctypes.c_int),
     "attn_fwd_varlen": ([_p, _p, _p, _p, _p, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _i64, _f32, _i32,
                          _p, _i32, _i32, _p, _sz, _p], ctypes.c_int),
+    "attn_fwd_noalloc": ([_p, _p, _p, _p, _p, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _i64, _f32, _i32, _p],
+                         ctypes.c_int),
     "attn_fwd_workspace_bytes": ([_i64, _i32, _i32, _i32], _sz),
     "attn_bwd_workspace_bytes": ([_i64, _i32, _i32, _i32, _i32], _sz),
     "attn_bwd": ([_p] * 9 + [_i64, _i32, _i32, _i32] + [_i64] * 8 + [_f32, _i32, _p, _sz, _p], ctypes.c_int),
@@ -286,6 +288,23 @@ def attn_fwd(q, k, v, o, lse, scale: float, causal: bool = True, cu_seqlens=None
     else:
         _check(_L.attn_fwd_varlen(*args, _ptr(cu_seqlens), n_seqs, int(max_seqlen or N), _ptr(ws), wsb, sh),
                "attn_fwd_varlen")
+
+
+# Bytes of the static scratch buffer attn_fwd_noalloc works in.
+NOALLOC_SCRATCH_BYTES = 80 << 20
+
+
+def attn_fwd_noalloc(q, k, v, o, lse, scale: float, causal: bool = True, stream=None) -> None:
+    """attn_fwd in the library's static per-GPU scratch buffer: no workspace
+    argument and no allocation (for callers that cannot allocate). Calls that
+    may overlap on one GPU race on that buffer."""
+    a = _Args("attn_fwd_noalloc")
+    N, hq, hkv, d = _qkv_dims(q, k)
+    strides = (a.rows(q, "q", N, hq, d), a.rows(k, "k", N, hkv, d), a.rows(v, "v", N, hkv, d),
+               a.rows(o, "o", N, hq, d))
+    a(lse, "lse", kind=torch.float32, shape=(hq, N), contiguous=True)
+    _check(_L.attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), N, hq, hkv, d, *strides,
+                               float(scale), int(bool(causal)), a.stream(stream)), "attn_fwd_noalloc")
 
 
 def attn_bwd_workspace_bytes(N: int, hq: int, hkv: int, d: int, n_seqs: int = 1) -> int:

@@ -4,8 +4,17 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "ulysses.h"
 #include "uly_internal.h"
+
+// Workspace of attn_fwd_noalloc, for callers that cannot allocate: one
+// static buffer per GPU, created when the library's code is loaded on that
+// GPU and held until the process ends. Host code never passes `scratch`
+// itself to a kernel (on the host it is only a stand-in for the symbol); it
+// passes the device address looked up once per device below.
+static __device__ __align__(256) unsigned char scratch[ULY_NOALLOC_SCRATCH_BYTES];
 
 namespace uly {
 
@@ -93,11 +102,34 @@ int check_varlen_args(const int32_t *cu, int32_t n_seqs, int32_t max_seqlen, int
   return ULY_OK;
 }
 
+// Device address of `scratch` on device `dev`, looked up once per device
+// with that device current (each GPU holds its own copy at its own address).
+constexpr int kMaxScratchDevices = 64;
+
+int scratch_address(int dev, void **out) {
+  static std::once_flag once[kMaxScratchDevices];
+  static void *addr[kMaxScratchDevices];
+  static hipError_t err[kMaxScratchDevices];
+  if (dev < 0 || dev >= kMaxScratchDevices) return set_error_text("attn_fwd_noalloc: device index out of range");
+  std::call_once(once[dev], [dev] {
+    int prev = 0;
+    err[dev] = hipGetDevice(&prev);
+    if (err[dev] == hipSuccess && prev != dev) err[dev] = hipSetDevice(dev);
+    if (err[dev] == hipSuccess) err[dev] = hipGetSymbolAddress(&addr[dev], HIP_SYMBOL(scratch));
+    if (prev != dev) (void)hipSetDevice(prev);
+  });
+  if (err[dev] != hipSuccess) return set_hip_error(err[dev], "attn_fwd_noalloc: hipGetSymbolAddress(scratch)");
+  *out = addr[dev];
+  return ULY_OK;
+}
+
+// ws == nullptr with use_scratch: the forward's workspace is the static
+// scratch buffer of the stream's device (attn_fwd_noalloc).
 int attn_fwd_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *o,
                   float *lse, int64_t N, int32_t hq, int32_t hkv, int32_t d, int64_t qs,
                   int64_t ks, int64_t vs, int64_t os, float scale, int32_t causal,
                   const int32_t *cu, int32_t n_seqs, void *ws, size_t ws_bytes,
-                  hipStream_t stream) {
+                  hipStream_t stream, bool use_scratch = false) {
   int rc = check_attn_common(q, k, v, N, hq, hkv, d, qs, ks, vs, scale);
   if (rc) return rc;
   if ((rc = check_out(o, N, os, (int64_t)hq * d))) return rc;
@@ -108,14 +140,21 @@ int attn_fwd_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint1
       overlaps(o, ob, v, span_bytes(N, vs, (int64_t)hkv * d)) ||
       overlaps(lse, (size_t)N * hq * 4, o, ob))
     return ULY_E_ALIAS;
-  if (!ws || ws_bytes < fwd_ws_bytes(N, hq, hkv, d) || (reinterpret_cast<uintptr_t>(ws) & 255u))
-    return ULY_E_WORKSPACE;
   const size_t wb = fwd_ws_bytes(N, hq, hkv, d);
-  if (overlaps(ws, wb, o, ob) || overlaps(ws, wb, lse, (size_t)N * hq * 4) ||
-      overlaps(ws, wb, q, span_bytes(N, qs, (int64_t)hq * d)) ||
-      overlaps(ws, wb, k, span_bytes(N, ks, (int64_t)hkv * d)) ||
-      overlaps(ws, wb, v, span_bytes(N, vs, (int64_t)hkv * d)))
-    return ULY_E_ALIAS;
+  if (use_scratch) {
+    if (wb > (size_t)ULY_NOALLOC_SCRATCH_BYTES) return ULY_E_SCRATCH;
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return set_hip_error(e, "attn_fwd_noalloc: device of the stream");
+    if ((rc = scratch_address(dev, &ws))) return rc;
+  } else {
+    if (!ws || ws_bytes < wb || (reinterpret_cast<uintptr_t>(ws) & 255u)) return ULY_E_WORKSPACE;
+    if (overlaps(ws, wb, o, ob) || overlaps(ws, wb, lse, (size_t)N * hq * 4) ||
+        overlaps(ws, wb, q, span_bytes(N, qs, (int64_t)hq * d)) ||
+        overlaps(ws, wb, k, span_bytes(N, ks, (int64_t)hkv * d)) ||
+        overlaps(ws, wb, v, span_bytes(N, vs, (int64_t)hkv * d)))
+      return ULY_E_ALIAS;
+  }
   AttnShape s;
   s.N = N;
   s.hq = hq;
@@ -225,6 +264,7 @@ const char *uly_status_string(int status) {
     case ULY_E_HIP: return "HIP error";
     case ULY_E_SEQLENS: return "invalid cu_seqlens";
     case ULY_E_ALIGN: return "pointer or stride not 16-byte aligned";
+    case ULY_E_SCRATCH: return "problem needs more than the static scratch buffer (ULY_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -274,6 +314,14 @@ int attn_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *
              size_t ws_bytes, hipStream_t stream) {
   return attn_fwd_impl(q, k, v, o, lse, N, hq, hkv, d, q_stride, k_stride, v_stride, o_stride,
                        scale, causal, nullptr, 0, ws, ws_bytes, stream);
+}
+
+int attn_fwd_noalloc(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *o,
+                     float *lse, int64_t N, int32_t hq, int32_t hkv, int32_t d, int64_t q_stride,
+                     int64_t k_stride, int64_t v_stride, int64_t o_stride, float scale,
+                     int32_t causal, hipStream_t stream) {
+  return attn_fwd_impl(q, k, v, o, lse, N, hq, hkv, d, q_stride, k_stride, v_stride, o_stride,
+                       scale, causal, nullptr, 0, nullptr, 0, stream, true);
 }
 
 int attn_fwd_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *o,

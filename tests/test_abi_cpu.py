@@ -105,6 +105,32 @@ def test_attn_fwd_validation(kw, code):
     assert _fwd(**kw) == uly.CODE[code]
 
 
+def test_attn_fwd_noalloc_validation():
+    """The allocation-free forward checks its arguments like attn_fwd and
+    rejects, before any device call, problems whose workspace exceeds its
+    static scratch buffer (80 MiB)."""
+    far = 1 << 36           # fake addresses far enough apart for 2^18 tokens
+
+    def fwd(N=1024, hq=8, hkv=2, o=4 * far, q=far, qs=1536):
+        return L.attn_fwd_noalloc(q, 2 * far, 3 * far, o, 5 * far, N, hq, hkv, 128, qs, qs, qs, hq * 128, 0.088,
+                                  1, None)
+
+    assert fwd(q=0) == uly.CODE["ULY_E_NULL"]
+    assert fwd(hkv=3) == uly.CODE["ULY_E_GQA"]
+    assert fwd(qs=1000) == uly.CODE["ULY_E_STRIDE"]
+    assert fwd(o=far) == uly.CODE["ULY_E_ALIAS"]
+    limit = uly.NOALLOC_SCRATCH_BYTES
+    assert limit == 80 << 20
+    # one KV head of 2^18 tokens fits (64 MiB of V^T); two heads at 2^18 or
+    # more tokens do not
+    assert L.attn_fwd_workspace_bytes(1 << 18, 4, 1, 128) <= limit
+    assert L.attn_fwd_workspace_bytes(1 << 18, 8, 2, 128) > limit
+    assert fwd(N=1 << 18, hq=8, hkv=2, qs=12 * 128) == uly.CODE["ULY_E_SCRATCH"]
+    assert L.attn_fwd_workspace_bytes(327680, 4, 1, 128) <= limit < L.attn_fwd_workspace_bytes(327744, 4, 1, 128)
+    assert fwd(N=327744, hq=4, hkv=1, qs=6 * 128) == uly.CODE["ULY_E_SCRATCH"]
+    assert "scratch" in uly.status_string(uly.CODE["ULY_E_SCRATCH"])
+
+
 def test_attn_varlen_and_bwd_validation():
     r = L.attn_fwd_varlen(A, B, C, D_, E, 1024, 8, 2, 128, 1536, 1536, 1536, 1024, 0.1, 1, None, 3, 512,
                           W, 1 << 25, None)
