@@ -258,10 +258,10 @@ int attn_bwd_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
  * Long Sequence Training"): dq sums over keys, dk and dv over queries, so
  * each step is one pass that recomputes the scores it needs.
  *
- * attn_bwd_dq: fills ws (D, LSE*log2(e), the transposed copies of K, Q and
- *   dO) and writes dq.
- * attn_bwd_dkdv: dk and dv. It reads D, LSE*log2(e) and the transposed
- *   copies of Q and dO from ws as left by attn_bwd_dq with the same
+ * attn_bwd_dq: fills ws (D, LSE*log2(e), the transposed copies of K and,
+ *   at d = 64, of Q and dO) and writes dq.
+ * attn_bwd_dkdv: dk and dv. It reads D, LSE*log2(e) and (d = 64) the
+ *   transposed copies of Q and dO from ws as left by attn_bwd_dq with the same
  *   arguments (not to be modified in between), and writes two other regions
  *   of ws: the order of its key blocks (packed documents) and its float32
  *   partial dK/dV (when it splits its query ranges, see

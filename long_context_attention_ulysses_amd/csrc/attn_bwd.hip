@@ -33,6 +33,16 @@
 #include "attn_common.h"
 #include "uly_internal.h"
 
+// Tiles the d = 128 dK/dV kernel copies ahead (1: tile t+1's copies land
+// while tile t is computed).
+#ifndef ULY_DKDV_PF
+#define ULY_DKDV_PF 1
+#endif
+// MFMAs' worth of transposing reads the dK and dV updates keep in flight.
+#ifndef ULY_TR_LA
+#define ULY_TR_LA 4
+#endif
+
 namespace uly {
 
 namespace {
@@ -341,15 +351,29 @@ struct DkvCfg {
 // dV product uses. Each wave then holds one of K or V and one of the dK or
 // dV accumulators, so a wave fits in 256 registers and two waves share each
 // SIMD: one's MFMAs run while the other computes exponentials or dS.
-template <int D, bool kSplit>
+//
+// kTr (d = 128): the dO^T and Q^T operands of the dV and dK products are
+// read from the Q and dO row tiles with transposing LDS reads (rt2 layout)
+// instead of being copied in from the transposed copies, which halves the
+// bytes copied into LDS per tile (Q and dO rows only). Q rows then live in a
+// 3-stage ring, since the deferred dK update reads tile t-1's while tile
+// t+1's arrive. Without kTr all four operands are copied (2-stage rings).
+template <int D, bool kSplit, bool kTr>
 __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs a) {
   using C = DkvCfg<D>;
-  __shared__ __align__(16) bf16_t q0s[C::TILE], q1s[C::TILE];    // Q row tiles
-  __shared__ __align__(16) bf16_t d0s[C::TILE], d1s[C::TILE];    // dO row tiles
-  __shared__ __align__(16) bf16_t qt0[C::TILE], qt1[C::TILE];    // Q^T trans tiles
-  __shared__ __align__(16) bf16_t dt0[C::TILE], dt1[C::TILE];    // dO^T trans tiles
-  __shared__ __align__(16) float ls0[2 * C::BQ], ls1[2 * C::BQ];  // LSE*log2e, D
-  __shared__ __align__(16) bf16_t xp[C::NKB * 4 * 512];          // P hand-over
+  static_assert(!kTr || D == 128, "the transposing-read layout is for d = 128");
+  // With kTr the copies of tile t + PF are issued at tile t; rows stay
+  // until their last reader: Q rows one tile longer (deferred dK update).
+  constexpr int PF = kTr ? ULY_DKDV_PF : 1;
+  constexpr int QST = kTr ? PF + 2 : 2;       // stages of the Q row ring
+  constexpr int DST = kTr ? PF + 1 : 2;       // stages of the dO row and LSE/D rings
+  constexpr int TT = kTr ? 8 : C::TILE;       // trans tiles (unused with kTr)
+  __shared__ __align__(16) bf16_t qrow[QST][C::TILE];   // Q row tiles
+  __shared__ __align__(16) bf16_t drow[DST][C::TILE];   // dO row tiles
+  __shared__ __align__(16) bf16_t qtt[2][TT];           // Q^T trans tiles
+  __shared__ __align__(16) bf16_t dtt[2][TT];           // dO^T trans tiles
+  __shared__ __align__(16) float lsb[DST][2 * C::BQ];   // LSE*log2e, D
+  __shared__ __align__(16) bf16_t xp[C::NKB * 4 * 512];  // P hand-over
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -414,6 +438,17 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
   const int tb = kSplit ? (int)((int64_t)ntiles * split / a.ksplit) : 0;
   const int te = kSplit ? (int)((int64_t)ntiles * (split + 1) / a.ksplit) : ntiles;
 
+  // Row-tile element offset of logical chunk c of row r, in the layout the
+  // Q and dO row tiles use.
+  auto roff = [](int r, int c) __attribute__((always_inline)) {
+    if constexpr (kTr) return rt2_off(r, c);
+    else return rt_off<D>(r, c);
+  };
+  auto rswz = [](int r) __attribute__((always_inline)) {
+    if constexpr (kTr) return rt2_swz(r);
+    else return row_swz<D>(r);
+  };
+
   // Per-lane byte offsets of this wave's 16-byte slots inside a tile: row
   // tiles of Q and dO (token stride), trans tiles of Q^T and dO^T.
   const uint32_t qsb = (uint32_t)(a.q_stride * 2), dsb = (uint32_t)(a.do_stride * 2);
@@ -422,12 +457,13 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
   for (int i = 0; i < C::NI / C::NW; ++i) {
     const int s = (w + i * C::NW) * 64 + lane;
     const int r = s / (D / 8);
-    const uint32_t cb = ((s % (D / 8)) ^ row_swz<D>(r)) << 4;
+    const uint32_t cb = ((s % (D / 8)) ^ rswz(r)) << 4;
     qoff[i] = r * qsb + cb;
     doff[i] = r * dsb + cb;
     const int d = s >> 3;
     toff[i] = (uint32_t)(d * a.Np * 2) + (((s & 7) ^ ((d >> 1) & 7)) << 4);
   }
+  [[maybe_unused]] const TrOffsets tro = kTr ? tr_offsets(lane) : TrOffsets{};
 
   // Tile t: query tiles from the last one down (every workgroup of a wave of
   // launches starts on the same tiles and walks them in step, so they are
@@ -435,9 +471,10 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
   auto tile_head = [&](int t) { return g * a.G + t % a.G; };
   auto tile_u0 = [&](int t) { return (uint32_t)(qt1_ - 1 - t / a.G) * C::BQ; };
 
-  // Copies of tile t: Q and dO row tiles, the dO^T trans tile and the
-  // tile's LSE*log2e and D (issue_rows); the Q^T trans tile (issue_qt),
-  // which is needed one tile later than the others (see the schedule below).
+  // Copies of tile t: Q and dO row tiles, the dO^T trans tile (without kTr)
+  // and the tile's LSE*log2e and D (issue_rows); the Q^T trans tile
+  // (issue_qt, without kTr), which is needed one tile later than the others
+  // (see the schedule below).
   auto issue_rows = [&](int t, bf16_t *qs, bf16_t *ds, bf16_t *dts, float *ls) {
     const int h = tile_head(t);
     const uint32_t u0 = tile_u0(t);
@@ -447,13 +484,19 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
                                  head_rows_bytes(a.N, a.q_stride, D) - u0 * qsb);
     const BufRes drs = make_rsrc(a.dout + (int64_t)u0 * a.do_stride + (int64_t)h * D,
                                  head_rows_bytes(a.N, a.do_stride, D) - u0 * dsb);
-    const BufRes dtr = make_rsrc(a.dot + (int64_t)h * D * a.Np, (uint32_t)(D * a.Np * 2));
 #pragma unroll
     for (int i = 0; i < C::NI / C::NW; ++i) {
       const int u = w + i * C::NW;
       dma16(qrs, qoff[i], 0, qs + u * 512);
       dma16(drs, doff[i], 0, ds + u * 512);
-      dma16(dtr, toff[i], u0 * 2, dts + u * 512);
+    }
+    if constexpr (!kTr) {
+      const BufRes dtr = make_rsrc(a.dot + (int64_t)h * D * a.Np, (uint32_t)(D * a.Np * 2));
+#pragma unroll
+      for (int i = 0; i < C::NI / C::NW; ++i) {
+        const int u = w + i * C::NW;
+        dma16(dtr, toff[i], u0 * 2, dts + u * 512);
+      }
     }
     if (w < 2) {  // wave 0: LSE*log2e of the 64 rows, wave 1: D; rows >= N read as zeros
       const float *src = (w == 0 ? a.lse2 : a.delta) + (int64_t)h * a.Np;
@@ -472,12 +515,12 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
     return wave_valid && u0 < w_hi && u0 + C::BQ > w_lo;
   };
 
-  // Schedule of tile t (stage t % 2 of every ring; B = ring barrier, X = P
-  // hand-over barrier):
-  //   wait for tile t's copies (all but Q^T(t)), B, issue_rows(t + 1)
+  // Schedule of tile t (stage t % 2 of every ring, t % 3 of the Q rows with
+  // kTr; B = ring barrier, X = P hand-over barrier):
+  //   wait for tile t's copies (without kTr: all but Q^T(t)), B, issue_rows(t + 1)
   //   phase 1  S role:  S(t), P(t), P -> LDS
   //            dP role: dK += Q^T(t-1) dS(t-1), dP(t)
-  //   X, issue_qt(t + 1) (its stage held Q^T(t-1), last read in phase 1)
+  //   X, without kTr: issue_qt(t + 1) (its stage held Q^T(t-1), last read in phase 1)
   //   phase 2  S role:  dV += dO^T(t) P(t)
   //            dP role: P(t) <- LDS, dS(t) (kept in registers for tile t+1)
   // Each phase pairs one wave's exponentials or dS arithmetic with its
@@ -488,29 +531,48 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
     bf16x8 sf[4];                                 // dP role: dS of the previous tile
     bool pend = false;                            // dP role: sf holds a tile not yet applied
 
+    // dK^T += Q^T(t-1) dS(t-1): Q^T from its trans tile, or (kTr) read
+    // transposed from tile t-1's Q rows.
     auto dk_update = [&](const bf16_t *qts) __attribute__((always_inline)) {
+      [[maybe_unused]] const uint32_t qa = lds_addr(qts);
 #pragma unroll
       for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-          const bf16x8 aqt = as_bf16x8(*reinterpret_cast<const u32x4 *>(qts + tr_off(db * 32 + l32, c * 2 + hi32)));
+          bf16x8 aqt;
+          if constexpr (kTr) aqt = tr_frag(qa, tro, db, c);
+          else aqt = as_bf16x8(*reinterpret_cast<const u32x4 *>(qts + tr_off(db * 32 + l32, c * 2 + hi32)));
           acc[db] = mfma32(aqt, sf[c], acc[db]);
         }
-      pipeline_reads_mfma<4 * C::DB>();
+      if constexpr (kTr) pipeline_reads_mfma_n<4 * C::DB, 2, ULY_TR_LA>();
+      else pipeline_reads_mfma<4 * C::DB>();
     };
 
+    // qs_prev: Q^T(t-1) trans tile, or (kTr) tile t-1's Q rows.
+    // qs_n, ds_n, ls_n: stages for tile t + PF's copies.
     auto tile = [&](int t, const bf16_t *qs, const bf16_t *ds, const bf16_t *dts, const float *ls,
-                    const bf16_t *qts_prev, bf16_t *qs_n, bf16_t *ds_n, bf16_t *dts_n, float *ls_n,
+                    const bf16_t *qs_prev, bf16_t *qs_n, bf16_t *ds_n, bf16_t *dts_n, float *ls_n,
                     bf16_t *qts_n) __attribute__((always_inline)) {
-      wait_vmcnt<C::NI / C::NW>();
+      if constexpr (kTr) {
+        // tile t's copies done; those of tiles t+1 .. t+PF-1 may be in flight
+        constexpr int per = 2 * (C::NI / C::NW);
+        if (t + PF - 1 < te) {
+          if (w < 2) wait_vmcnt<(PF - 1) * (per + 1)>();
+          else wait_vmcnt<(PF - 1) * per>();
+        } else {
+          wait_vmcnt<0>();
+        }
+      } else {
+        wait_vmcnt<C::NI / C::NW>();
+      }
       barrier();
-      if (t + 1 < te) issue_rows(t + 1, qs_n, ds_n, dts_n, ls_n);
+      if (t + PF < te) issue_rows(t + PF, qs_n, ds_n, dts_n, ls_n);
       const int64_t u0 = tile_u0(t);
       const bool act = active(t);
       f32x16 x[2];
       bf16x8 pf[4];
       if constexpr (!S) {
-        if (pend) dk_update(qts_prev);
+        if (pend) dk_update(qs_prev);
       }
       if (act) {
 #pragma unroll
@@ -523,7 +585,7 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
             const bf16x8 ar =
-                as_bf16x8(*reinterpret_cast<const u32x4 *>(rows + rt_off<D>(q * 32 + l32, ks * 2 + hi32)));
+                as_bf16x8(*reinterpret_cast<const u32x4 *>(rows + roff(q * 32 + l32, ks * 2 + hi32)));
             x[q] = mfma32(ar, xf[ks], x[q]);
           }
         pipeline_reads_mfma<2 * C::KS>();
@@ -557,18 +619,23 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
         }
       }
       lds_barrier();
-      if (t + 1 < te) issue_qt(t + 1, qts_n);
+      if constexpr (!kTr) {
+        if (t + 1 < te) issue_qt(t + 1, qts_n);
+      }
       if constexpr (S) {
         if (act) {
+          [[maybe_unused]] const uint32_t da = lds_addr(ds);
 #pragma unroll
           for (int c = 0; c < 4; ++c)
 #pragma unroll
             for (int db = 0; db < C::DB; ++db) {
-              const bf16x8 adt =
-                  as_bf16x8(*reinterpret_cast<const u32x4 *>(dts + tr_off(db * 32 + l32, c * 2 + hi32)));
+              bf16x8 adt;
+              if constexpr (kTr) adt = tr_frag(da, tro, db, c);
+              else adt = as_bf16x8(*reinterpret_cast<const u32x4 *>(dts + tr_off(db * 32 + l32, c * 2 + hi32)));
               acc[db] = mfma32(adt, pf[c], acc[db]);
             }
-          pipeline_reads_mfma<4 * C::DB>();
+          if constexpr (kTr) pipeline_reads_mfma_n<4 * C::DB, 2, ULY_TR_LA>();
+          else pipeline_reads_mfma<4 * C::DB>();
         }
       } else {
         pend = act;
@@ -598,20 +665,37 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
     };
 
     wait_vmcnt<0>();  // K or V fragments loaded: only tile copies are counted below
-    if (tb < te) {
-      issue_rows(tb, q0s, d0s, dt0, ls0);
-      issue_qt(tb, qt0);
-    }
-    for (int t = tb; t < te; t += 2) {
-      tile(t, q0s, d0s, dt0, ls0, qt1, q1s, d1s, dt1, ls1, qt1);
-      if (t + 1 < te) tile(t + 1, q1s, d1s, dt1, ls1, qt0, q0s, d0s, dt0, ls0, qt0);
-    }
-    // The last tile's dK update: its Q^T copy is complete once every wave
-    // has waited for its own part of it.
-    wait_vmcnt<0>();
-    barrier();
-    if constexpr (!S) {
-      if (pend) dk_update((te - 1 - tb) % 2 == 0 ? qt0 : qt1);
+    if constexpr (kTr) {
+#pragma unroll
+      for (int p = 0; p < PF; ++p)
+        if (tb + p < te) issue_rows(tb + p, qrow[p], drow[p], nullptr, lsb[p]);
+      for (int t = tb; t < te; ++t) {
+        const int rel = t - tb;
+        const int qi = rel % QST, di = rel % DST;
+        const int qn = (rel + PF) % QST, dn = (rel + PF) % DST;
+        tile(t, qrow[qi], drow[di], nullptr, lsb[di], qrow[qi == 0 ? QST - 1 : qi - 1], qrow[qn], drow[dn], nullptr,
+             lsb[dn], nullptr);
+      }
+      // The last tile's dK update (its Q rows stay in place: nothing more is copied).
+      if constexpr (!S) {
+        if (pend) dk_update(qrow[(te - 1 - tb) % QST]);
+      }
+    } else {
+      if (tb < te) {
+        issue_rows(tb, qrow[0], drow[0], dtt[0], lsb[0]);
+        issue_qt(tb, qtt[0]);
+      }
+      for (int t = tb; t < te; t += 2) {
+        tile(t, qrow[0], drow[0], dtt[0], lsb[0], qtt[1], qrow[1], drow[1], dtt[1], lsb[1], qtt[1]);
+        if (t + 1 < te) tile(t + 1, qrow[1], drow[1], dtt[1], lsb[1], qtt[0], qrow[0], drow[0], dtt[0], lsb[0], qtt[0]);
+      }
+      // The last tile's dK update: its Q^T copy is complete once every wave
+      // has waited for its own part of it.
+      wait_vmcnt<0>();
+      barrier();
+      if constexpr (!S) {
+        if (pend) dk_update((te - 1 - tb) % 2 == 0 ? qtt[0] : qtt[1]);
+      }
     }
   };
   if (srole)
@@ -790,12 +874,13 @@ int launch_dkdv_cfg(BwdArgs a, hipStream_t stream) {
                                           const_cast<int32_t *>(a.korder), stream);
     if (rc) return rc;
   }
+  constexpr bool kTr = D == 128;
   if (a.ksplit > 1)
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true>), dim3((unsigned)((int64_t)a.nblk * a.hkv * a.ksplit)),
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true, kTr>), dim3((unsigned)((int64_t)a.nblk * a.hkv * a.ksplit)),
                        dim3(C::NT), 0, stream, a);
   else
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false>), dim3((unsigned)((int64_t)a.nblk * a.hkv)), dim3(C::NT),
-                       0, stream, a);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false, kTr>), dim3((unsigned)((int64_t)a.nblk * a.hkv)),
+                       dim3(C::NT), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_hip_error(e, "attn_bwd_dkdv_kernel");
   if (a.ksplit > 1) {
@@ -869,8 +954,10 @@ int launch_attn_bwd(const AttnShape &s, const AttnBwdPtrs &p, int parts, hipStre
     bf16_t *ws_qt = reinterpret_cast<bf16_t *>(p.ws + L.qt);
     bf16_t *ws_dot = reinterpret_cast<bf16_t *>(p.ws + L.dot);
     if ((rc = launch_to_trans(p.k, s.k_stride, s.hkv, s.d, s.N, ws_kt, stream))) return rc;
-    if ((rc = launch_to_trans(p.q, s.q_stride, s.hq, s.d, s.N, ws_qt, stream))) return rc;
-    if ((rc = launch_to_trans(p.dout, p.do_stride, s.hq, s.d, s.N, ws_dot, stream))) return rc;
+    if (s.d != 128) {  // at d = 128 the dK/dV kernel reads Q and dO rows transposed in LDS
+      if ((rc = launch_to_trans(p.q, s.q_stride, s.hq, s.d, s.N, ws_qt, stream))) return rc;
+      if ((rc = launch_to_trans(p.dout, p.do_stride, s.hq, s.d, s.N, ws_dot, stream))) return rc;
+    }
     if (s.d == 128)
       rc = hpw == 4 ? launch_dq_cfg<128, 4, 2>(a, stream)
            : hpw == 2 ? launch_dq_cfg<128, 2, 4>(a, stream)

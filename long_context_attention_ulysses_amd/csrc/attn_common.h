@@ -76,6 +76,68 @@ __device__ __forceinline__ int rt_off(int r, int c) {
 // a trans tile.
 __device__ __forceinline__ int tr_off(int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 7)) << 3); }
 
+// ---- Row tiles read both ways (d = 128) ------------------------------------
+// A [64 rows][128] row tile that is read both as the [row][k] operand (16
+// consecutive rows at one 16-byte chunk, as above) and, transposed, as the
+// [d][row] operand of a product that contracts over its rows. The
+// transposed operand comes from ds_read_b64_tr_b16: in each group of 16
+// lanes, lane i receives element i % 4 of the 8-byte pieces that lanes
+// i / 4 + 4 j (j = 0..3) point at. With lane s of the group pointing at row
+// base + s / 4, elements 4 (s % 4) .. +3 of a 16-column block, lane i
+// receives column i of rows base .. base + 3: four consecutive rows of one
+// column, as the MFMA operand needs. Two such reads give the eight rows of
+// one 16-position contraction step, in the contraction order of the score
+// registers (positions 8 h + e hold rows 16 c + 8 (e / 4) + 4 h + e % 4).
+// The swizzle swaps the two 2-bit halves of the row's low 4 bits, so that
+// both the 16 rows of a row read and the 4 rows x 4 chunks of the 32 lanes
+// of a transposing read land on distinct banks.
+__device__ __forceinline__ int rt2_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// Element offset of logical 16-byte chunk c of row r.
+__device__ __forceinline__ int rt2_off(int r, int c) { return r * 128 + ((c ^ rt2_swz(r)) << 3); }
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// One transposing 8-byte LDS read at LDS byte address `addr`.
+__device__ __forceinline__ u32x2 ds_read_tr(uint32_t addr) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(uintptr_t)addr);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Per-lane byte offsets, inside a row tile, of the two transposing reads
+// (r = 0, 1) that make the [32 d][16 rows] operand for d block db and the
+// first 16-row step; step c adds 4096 c bytes.
+struct TrOffsets {
+  uint32_t off[2][4];
+};
+
+__device__ __forceinline__ TrOffsets tr_offsets(int lane) {
+  const int hi = lane >> 5, y = (lane & 15) >> 2, x = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1), h = lane & 1;
+  TrOffsets t;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int m = (y << 2) ^ (2 * r + hi) ^ x;  // chunk 4 db + x of row 8 r + 4 hi + y, swizzled
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+      t.off[r][db] = (uint32_t)(((8 * r + 4 * hi + y) * 128 + (((4 * db) ^ m) << 3) + 4 * h) * 2);
+  }
+  return t;
+}
+
+// The transposed operand (A[m = d][k = row]) for d block db and 16-row step
+// c of the row tile at LDS byte address `tile`.
+__device__ __forceinline__ bf16x8 tr_frag(uint32_t tile, const TrOffsets &t, int db, int c) {
+  const u32x2 lo = ds_read_tr(tile + t.off[0][db] + 4096 * c);
+  const u32x2 hi = ds_read_tr(tile + t.off[1][db] + 4096 * c);
+  u32x4 v;
+  v[0] = lo[0];
+  v[1] = lo[1];
+  v[2] = hi[0];
+  v[3] = hi[1];
+  return as_bf16x8(v);
+}
+
 // Buffer resource (four SGPRs) over the `bytes` bytes at `base`: buffer
 // loads at byte offsets >= bytes return zeros (raw buffer, stride 0).
 typedef uint32_t BufRes __attribute__((ext_vector_type(4)));
@@ -194,6 +256,19 @@ __device__ __forceinline__ void pipeline_reads_mfma() {
   for (int i = 0; i < NR - LA; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
+}
+
+// The same for blocks whose MFMAs take RPM LDS reads each: LA MFMAs'
+// worth of reads first, then one MFMA and its next RPM reads alternately.
+template <int NM, int RPM, int LA = 4>
+__device__ __forceinline__ void pipeline_reads_mfma_n() {
+  __builtin_amdgcn_sched_group_barrier(0x100, LA * RPM, 0);
+#pragma unroll
+  for (int i = 0; i < NM - LA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
 }
