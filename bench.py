@@ -27,6 +27,7 @@ if ROOT not in sys.path:
 METRIC = "attn fwd+bwd TFLOP/s (% bf16 MFMA peak) at 64K head-shard; swap GB/s"
 BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
+PEAK_CLOCK_GHZ = 2.4        # the engine clock the published bf16 peak assumes
 
 
 def log(*a):
@@ -86,18 +87,16 @@ KERNEL_OF = {"a3_attn_fwd": "attn_fwd_kernel", "a7a9_attn_bwd_dq": "attn_bwd_dq_
              "a8_attn_bwd_dkdv": "attn_bwd_dkdv_kernel"}
 
 
-def swap_cold_warm(uly, torch, x_seq, send, P, segments, reps=10):
-    """The a1 pack timed alone, outside the step: cold (a 512 MiB scratch
-    write between repetitions evicts the MALL) and warm (back to back),
-    medians of `reps`, with a device-to-device copy of the same bytes as the
-    achievable-copy reference. Bytes counted: one read + one write."""
+def swap_cold_warm(torch, fns, reps=10):
+    """Each swap timed alone, outside the step: cold (a 512 MiB scratch write
+    between repetitions evicts the MALL) and warm (back to back), medians of
+    `reps`, each beside a device-to-device copy of the same bytes as the
+    achievable-copy reference. Bytes counted: one read + one write.
+    fns: {name: (launch, src, dst)} with src/dst the swap's tensors."""
     import numpy as np
-    nbytes = 2 * x_seq.numel() * x_seq.element_size()
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-    flat_src = x_seq.view(-1)
-    flat_dst = send.view(-1)
 
-    def timed(fn, cold):
+    def timed(fn, nbytes, cold):
         ts = []
         for _ in range(reps):
             if cold:
@@ -110,17 +109,21 @@ def swap_cold_warm(uly, torch, x_seq, send, P, segments, reps=10):
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1))
         ms = float(np.median(ts))
-        return {"ms": round(ms, 4), "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+        return {"ms": round(ms, 4), "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
 
-    pack = lambda: uly.ulysses_seq_to_head(x_seq, send, P, segments)
-    copy = lambda: flat_dst.copy_(flat_src)
-    out = {"bytes": nbytes, "pack_cold": timed(pack, True), "pack_warm": timed(pack, False),
-           "d2d_copy_cold": timed(copy, True), "d2d_copy_warm": timed(copy, False)}
+    out = {}
+    for name, (launch, src, dst) in fns.items():
+        nbytes = 2 * src.numel() * src.element_size()
+        flat_src, flat_dst = src.reshape(-1), dst.view(-1)
+        copy = lambda: flat_dst.copy_(flat_src)  # noqa: E731
+        out[name] = {"bytes": nbytes, "cold": timed(launch, nbytes, True), "warm": timed(launch, nbytes, False),
+                     "d2d_copy_cold": timed(copy, nbytes, True), "d2d_copy_warm": timed(copy, nbytes, False)}
     del scratch
     return out
 
 
-def ring_step(uly, torch, w, x_seq, dy_seq, reps=3):
+def ring_step(uly, torch, w, reps=3):
     """Ring attention at the same sequence and P: rank P-1 (the one with the
     most work) attends its n tokens x all Hq heads to all P key/value blocks
     (its own block causal, the P-1 earlier ones unmasked), merges the P
@@ -128,6 +131,11 @@ def ring_step(uly, torch, w, x_seq, dy_seq, reps=3):
     the P dQ shares. Every block reuses the rank's own q|k|v data (timing does
     not depend on the values). Medians over `reps`."""
     import numpy as np
+
+    import workloads
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()  # noqa: E731
+    x_seq = dev(workloads.gen_seq_shard(w, 0))
+    dy_seq = dev(workloads.gen_dy_seq_shard(w, 0))
     P, n, Hq, Hkv, d = w.P, w.n, w.Hq, w.Hkv, w.d
     q, k, v = x_seq[:, :Hq], x_seq[:, Hq:Hq + Hkv], x_seq[:, Hq + Hkv:]
     o_parts = [torch.empty((n, Hq, d), dtype=torch.int16, device="cuda") for _ in range(P)]
@@ -292,130 +300,14 @@ def mlp_step(uly, torch, w, tile=4096, reps=3):
     return out
 
 
-def csrc_digest():
-    """sha256 over the HIP sources (names and bytes), to tell whether stored
-    counter readings still describe the kernels being run."""
-    import glob
-    import hashlib
-    h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "long_context_attention_ulysses_amd", "csrc", "*"))):
-        h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()
-
-
-def measured_traffic(workload: str, step_name: str):
-    """HBM bytes per launch of a kernel from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE summary (profiles/traffic_<workload>.txt, counters scaled by the
-    readings of a copy of known size), or None when there is no summary for
-    this workload or the kernels changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", "traffic_%s.txt" % workload)
-    if not os.path.exists(path):
-        return None
-    with open(path) as fh:
-        doc = json.load(fh)
-    if doc.get("source_sha256") != csrc_digest():
-        return None
-    prefix = KERNEL_OF[step_name]
-    hits = [d["hbm_bytes"] for d in doc["dispatches"] if d["kernel"].startswith(prefix)]
-    return hits[0] if len(hits) == 1 else None
-
-
-def short_kernel_name(full: str) -> str:
-    """'void uly::(anonymous namespace)::f<128, 4>(args)' -> 'f<128, 4>'."""
-    name = full.replace("(anonymous namespace)::", "")
-    name = name.split("(")[0].replace("void ", "", 1)
-    return name.split("::")[-1].strip()
-
-
-def write_traffic_summary(workload: str, pmc_dir: str):
-    """Turn two rocprofv3 counter runs of `bench.py --steps 1 --warmup 0`
-    (FETCH_SIZE in <pmc_dir>/fetch_counter_collection.csv, WRITE_SIZE in
-    <pmc_dir>/write_counter_collection.csv) into profiles/traffic_<workload>.txt.
-    Both counters are scaled by what they read for the step's first launch,
-    the seq->head pack, which reads and writes exactly the sequence shard's
-    bytes once."""
-    import csv
-
-    import workloads
-    w = workloads.WORKLOADS[workload]
-
-    def read(name, counter):
-        rows = []
-        with open(os.path.join(pmc_dir, "%s_counter_collection.csv" % name)) as fh:
-            for r in csv.DictReader(fh):
-                assert r["Counter_Name"] == counter, r["Counter_Name"]
-                rows.append((int(r["Dispatch_Id"]), short_kernel_name(r["Kernel_Name"]),
-                             float(r["Counter_Value"])))
-        return sorted(rows)
-
-    fetch, write = read("fetch", "FETCH_SIZE"), read("write", "WRITE_SIZE")
-    assert [(d, k) for d, k, _ in fetch] == [(d, k) for d, k, _ in write], "runs launched different kernels"
-    shard_bytes = w.n * w.Ht * w.d * 2
-    assert fetch[0][1].startswith("swap"), fetch[0][1]
-    fetch_scale = shard_bytes / (fetch[0][2] * 1024)
-    write_scale = shard_bytes / (write[0][2] * 1024)
-    doc = {
-        "workload": "%s head shard, one bench step (--steps 1 --warmup 0)" % workload,
-        "commands": [
-            "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $PMC -o fetch "
-            "-- python3 $REPO/bench.py --workload %s --steps 1 --warmup 0 --cpu-tokens 0 --no-ring --no-loss --no-mlp" % workload,
-            "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $PMC -o write "
-            "-- python3 $REPO/bench.py --workload %s --steps 1 --warmup 0 --cpu-tokens 0 --no-ring --no-loss --no-mlp" % workload,
-            "python3 $REPO/bench.py --workload %s --traffic-summary $PMC" % workload,
-        ],
-        "calibration": {
-            "kernel": "%s (a1 pack of the %d x %d x %d bf16 sequence shard: reads and writes exactly %d bytes)"
-                      % (fetch[0][1], w.n, w.Ht, w.d, shard_bytes),
-            "fetch_scale": fetch_scale,
-            "write_scale": write_scale,
-        },
-        "source_sha256": csrc_digest(),
-        "dispatches": [
-            {"dispatch": d, "kernel": k, "fetch_kb": fv, "write_kb": wv,
-             "hbm_bytes": int(round((fv * fetch_scale + wv * write_scale) * 1024))}
-            for (d, k, fv), (_, _, wv) in zip(fetch, write)
-        ],
-    }
-    out = os.path.join(ROOT, "profiles", "traffic_%s.txt" % workload)
-    with open(out, "w") as fh:
-        json.dump(doc, fh, indent=1)
-        fh.write("\n")
-    log("wrote %s" % out)
-
-
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="64k", choices=["tiny", "8k", "64k", "varlen", "256k"])
-    ap.add_argument("--cpu-tokens", type=int, default=9216,
-                    help="tokens of the oracle's CPU-baseline sample (0 = skip)")
-    ap.add_argument("--no-ring", action="store_true", help="skip the ring-attention measurement")
-    ap.add_argument("--no-loss", action="store_true", help="skip the shifted-label loss measurement")
-    ap.add_argument("--no-mlp", action="store_true", help="skip the TiledMLP measurement")
-    ap.add_argument("--traffic-summary", metavar="PMC_DIR",
-                    help="write profiles/traffic_<workload>.txt from two rocprofv3 counter runs and exit")
-    args = ap.parse_args()
-    if args.traffic_summary:
-        write_traffic_summary(args.workload, args.traffic_summary)
-        return
-
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU's share of the Ulysses path; runs on more than one GPU "
-              "are not supported: the exchange between GPUs is not implemented (requested --gpus %d)" % args.gpus, file=sys.stderr)
-        sys.exit(2)
-
+def measure_workload(uly, torch, w, steps, warmup, swaps_alone):
+    """One workload's step (a1, a3, a5, a6, a7+a9, a8, a10 on inputs already
+    resident in HBM): `warmup` untimed steps, then `steps` timed between two
+    synchronizations; per-kernel times from HIP events recorded on the
+    launch stream (torch's current stream, which the library launches on)."""
     import numpy as np
-    import torch
 
-    import long_context_attention_ulysses_amd as uly
     import workloads
-
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    w = workloads.WORKLOADS[args.workload]
     cu = workloads.cu_seqlens(w) if w.varlen else None
     log("workload %s: N=%d P=%d hq=%d hkv=%d d=%d" % (w.name, w.N, w.P, w.hq, w.hkv, w.d))
 
@@ -471,8 +363,7 @@ def main():
     }
     total_flops = 14.0 * d * U * hq
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-              for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
 
     def step(ev=None):
         if ev is not None:
@@ -482,58 +373,48 @@ def main():
             if ev is not None:
                 ev[i + 1].record()
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step()
         torch.cuda.synchronize()
         log("warmup step %d done" % (i + 1))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(events[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    log("timed %d steps: %.3f ms/step" % (args.steps, ms_per_step))
+    ms_per_step = (t1 - t0) * 1e3 / steps
+    log("timed %d steps: %.3f ms/step" % (steps, ms_per_step))
 
-    kern_all = {nm: [events[s][i].elapsed_time(events[s][i + 1]) for s in range(args.steps)]
+    kern_all = {nm: [events[s_][i].elapsed_time(events[s_][i + 1]) for s_ in range(steps)]
                 for i, nm in enumerate(names)}
-    kern_ms = {nm: float(np.mean(v)) for nm, v in kern_all.items()}
-    kern_med = {nm: float(np.median(v)) for nm, v in kern_all.items()}
-    peak_mem = torch.cuda.max_memory_allocated()
+    kern_ms = {nm: float(np.mean(v_)) for nm, v_ in kern_all.items()}
+    kern_med = {nm: float(np.median(v_)) for nm, v_ in kern_all.items()}
     attn_ms = kern_ms["a3_attn_fwd"] + kern_ms["a7a9_attn_bwd_dq"] + kern_ms["a8_attn_bwd_dkdv"]
     swap_gbps = {nm: swap_bytes[nm] / (kern_ms[nm] * 1e-3) / 1e9 for nm in swap_bytes}
     dom = max(flops, key=lambda nm: kern_ms[nm])
     achieved = flops[dom] / (kern_ms[dom] * 1e-3) / 1e12
     value = total_flops / (ms_per_step * 1e-3) / 1e12
 
-    result = {
-        "metric": METRIC,
-        "value": round(value, 3),
+    roofline = {
+        "kernel": dom,
+        "bound": "mfma",
+        "achieved": round(achieved, 2),
+        "peak": BF16_PEAK_TFLOPS,
         "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+        "traffic": None,
+    }
+    out = {
+        "value": round(value, 3),
         "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
         "config": {
             "workload": "Qwen3-4B-shaped SP=%d head shard, %s: N=%d tokens, %d q / %d kv heads, d=%d, causal%s"
                         % (P, w.name, w.N, hq, hkv, d, ", packed docs" if cu is not None else ""),
             "N": w.N, "P": P, "hq": hq, "hkv": hkv, "d": d, "seq_shard": [n, w.Ht, d],
             "n_docs": None if cu is None else len(cu) - 1,
         },
-        "roofline": {
-            "kernel": dom,
-            "bound": "mfma",
-            "achieved": round(achieved, 2),
-            "peak": BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-            "traffic": measured_traffic(args.workload, dom),
-        },
+        "roofline": roofline,
         "attn_tflops": round(total_flops / (attn_ms * 1e-3) / 1e12, 2),
         "attn_frac_peak": round(total_flops / (attn_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
         "value_frac_peak": round(value / BF16_PEAK_TFLOPS, 4),
@@ -547,13 +428,224 @@ def main():
         "swap_gbps": {k_: round(v_, 1) for k_, v_ in swap_gbps.items()},
         "swap_frac_hbm": {k_: round(v_ / HBM_PEAK_GBPS, 4) for k_, v_ in swap_gbps.items()},
         "counted_flop_per_step": total_flops,
-        "peak_device_bytes": peak_mem,
+        "peak_device_bytes": torch.cuda.max_memory_allocated(),
         "unmasked_pairs_per_head": U,
     }
-    result["swap_a1_alone"] = swap_cold_warm(uly, torch, x_seq, send, P, w.segments)
+    if swaps_alone:
+        out["swaps_alone"] = swap_cold_warm(torch, {
+            "a1_pack_qkv": (launches[0], x_seq, send),
+            "a5_unpack_o": (launches[2], o_chunks, o_seq),
+            "a6_pack_do": (launches[3], dy_seq, dsend),
+            "a10_unpack_dqkv": (launches[6], g_chunks, dqkv_seq),
+        })
+    del x_seq, recv, dy_seq, dy_head, send, o, lse, o_seq, dsend, dqkv, dqkv_seq, ws, ws_fwd
+    torch.cuda.empty_cache()
+    return out
+
+
+def csrc_digest():
+    """sha256 over the HIP sources (names and bytes), to tell whether stored
+    counter readings still describe the kernels being run."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "long_context_attention_ulysses_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_profile(workload: str, step_name: str):
+    """What the committed rocprofv3 counter summary (profiles/traffic_<workload>.txt)
+    says about a kernel's first dispatch in the profiled step: HBM bytes
+    (FETCH_SIZE + WRITE_SIZE, scaled by the readings of a copy of known size)
+    and the engine clock (GRBM_GUI_ACTIVE cycles over the 8 XCDs / the
+    dispatch's duration). None when there is no summary for this workload or
+    the HIP sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.txt" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        doc = json.load(fh)
+    if doc.get("source_sha256") != csrc_digest():
+        return None
+    prefix = KERNEL_OF[step_name]
+    # the first dispatch of the kernel is the one in the profiled step
+    hits = [d for d in doc["dispatches"] if d["kernel"].startswith(prefix)]
+    if not hits:
+        return None
+    out = {"hbm_bytes": hits[0]["hbm_bytes"]}
+    if hits[0].get("clock_ghz"):
+        out["clock_ghz"] = hits[0]["clock_ghz"]
+        out["clock_source"] = ("GRBM_GUI_ACTIVE / 8 XCDs / kernel duration of the same dispatch "
+                               "(profiles/traffic_%s.txt)" % workload)
+    return out
+
+
+def short_kernel_name(full: str) -> str:
+    """'void uly::(anonymous namespace)::f<128, 4>(args)' -> 'f<128, 4>'."""
+    name = full.replace("(anonymous namespace)::", "")
+    name = name.split("(")[0].replace("void ", "", 1)
+    return name.split("::")[-1].strip()
+
+
+def write_traffic_summary(workload: str, pmc_dir: str):
+    """Turn the rocprofv3 counter runs of `bench.py --steps 1 --warmup 0`
+    into profiles/traffic_<workload>.txt:
+      - FETCH_SIZE in <pmc_dir>/fetch_counter_collection.csv and WRITE_SIZE in
+        <pmc_dir>/write_counter_collection.csv: HBM bytes per dispatch. Both
+        counters are scaled by what they read for the step's first launch,
+        the seq->head pack, which reads and writes exactly the sequence
+        shard's bytes once.
+      - optionally GRBM_GUI_ACTIVE with the kernel trace of the same run
+        (<pmc_dir>/grbm_counter_collection.csv, grbm_kernel_trace.csv): the
+        engine clock of each dispatch, as its busy cycles summed over the 8
+        XCDs / 8 / its duration."""
+    import csv
+
+    import workloads
+    w = workloads.WORKLOADS[workload]
+
+    def read(name, counter):
+        rows = []
+        with open(os.path.join(pmc_dir, "%s_counter_collection.csv" % name)) as fh:
+            for r in csv.DictReader(fh):
+                assert r["Counter_Name"] == counter, r["Counter_Name"]
+                rows.append((int(r["Dispatch_Id"]), short_kernel_name(r["Kernel_Name"]),
+                             float(r["Counter_Value"])))
+        return sorted(rows)
+
+    fetch, write = read("fetch", "FETCH_SIZE"), read("write", "WRITE_SIZE")
+    assert [(d, k) for d, k, _ in fetch] == [(d, k) for d, k, _ in write], "runs launched different kernels"
+    clocks = {}
+    grbm_path = os.path.join(pmc_dir, "grbm_counter_collection.csv")
+    if os.path.exists(grbm_path):
+        grbm = read("grbm", "GRBM_GUI_ACTIVE")
+        assert [(d, k) for d, k, _ in grbm] == [(d, k) for d, k, _ in fetch], "runs launched different kernels"
+        dur = {}
+        with open(os.path.join(pmc_dir, "grbm_kernel_trace.csv")) as fh:
+            for r in csv.DictReader(fh):
+                dur[int(r["Dispatch_Id"])] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        for d, _, cyc in grbm:
+            if dur.get(d, 0) > 0:
+                clocks[d] = (cyc / 8.0 / dur[d], dur[d])   # cycles per ns = GHz
+    shard_bytes = w.n * w.Ht * w.d * 2
+    assert fetch[0][1].startswith("swap"), fetch[0][1]
+    fetch_scale = shard_bytes / (fetch[0][2] * 1024)
+    write_scale = shard_bytes / (write[0][2] * 1024)
+    run = ("-- python3 $REPO/bench.py --workload %s --steps 1 --warmup 0 --cpu-tokens 0 --no-ring --no-loss "
+           "--no-mlp --no-workloads" % workload)
+    doc = {
+        "workload": "%s head shard, one bench step (--steps 1 --warmup 0)" % workload,
+        "commands": [
+            "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $PMC -o fetch " + run,
+            "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $PMC -o write " + run,
+            "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc GRBM_GUI_ACTIVE --kernel-trace --output-format csv "
+            "-d $PMC -o grbm " + run,
+            "python3 $REPO/bench.py --workload %s --traffic-summary $PMC" % workload,
+        ],
+        "calibration": {
+            "kernel": "%s (a1 pack of the %d x %d x %d bf16 sequence shard: reads and writes exactly %d bytes)"
+                      % (fetch[0][1], w.n, w.Ht, w.d, shard_bytes),
+            "fetch_scale": fetch_scale,
+            "write_scale": write_scale,
+        },
+        "host": os.uname().nodename,
+        "source_sha256": csrc_digest(),
+        "dispatches": [],
+    }
+    for (d, k, fv), (_, _, wv) in zip(fetch, write):
+        e = {"dispatch": d, "kernel": k, "fetch_kb": fv, "write_kb": wv,
+             "hbm_bytes": int(round((fv * fetch_scale + wv * write_scale) * 1024))}
+        if d in clocks:
+            e["clock_ghz"] = round(clocks[d][0], 4)
+            e["duration_ns"] = clocks[d][1]
+        doc["dispatches"].append(e)
+    out = os.path.join(ROOT, "profiles", "traffic_%s.txt" % workload)
+    with open(out, "w") as fh:
+        json.dump(doc, fh, indent=1)
+        fh.write("\n")
+    log("wrote %s" % out)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="64k", choices=["tiny", "8k", "64k", "varlen", "256k"])
+    ap.add_argument("--cpu-tokens", type=int, default=9216,
+                    help="tokens of the oracle's CPU-baseline sample (0 = skip)")
+    ap.add_argument("--no-ring", action="store_true", help="skip the ring-attention measurement")
+    ap.add_argument("--no-loss", action="store_true", help="skip the shifted-label loss measurement")
+    ap.add_argument("--no-mlp", action="store_true", help="skip the TiledMLP measurement")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the short runs of the 8k, varlen and 256k workloads after the 64k one")
+    ap.add_argument("--traffic-summary", metavar="PMC_DIR",
+                    help="write profiles/traffic_<workload>.txt from two rocprofv3 counter runs and exit")
+    args = ap.parse_args()
+    if args.traffic_summary:
+        write_traffic_summary(args.workload, args.traffic_summary)
+        return
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU's share of the Ulysses path; runs on more than one GPU "
+              "are not supported: the exchange between GPUs is not implemented (requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import long_context_attention_ulysses_amd as uly
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = workloads.WORKLOADS[args.workload]
+    cu = workloads.cu_seqlens(w) if w.varlen else None
+    r = measure_workload(uly, torch, w, args.steps, args.warmup, swaps_alone=True)
+    result = {
+        "metric": METRIC,
+        "value": r["value"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": r.pop("config"),
+    }
+    prof = measured_profile(args.workload, r["roofline"]["kernel"])
+    r["roofline"]["traffic"] = prof and prof["hbm_bytes"]
+    if prof and prof.get("clock_ghz"):
+        # clock measured by the committed counter pass of the same sources
+        ghz = prof["clock_ghz"]
+        r["roofline"]["clock_ghz"] = ghz
+        r["roofline"]["peak_at_clock"] = round(BF16_PEAK_TFLOPS * ghz / PEAK_CLOCK_GHZ, 1)
+        r["roofline"]["frac_clock_adjusted"] = round(r["roofline"]["achieved"] / r["roofline"]["peak_at_clock"], 4)
+        r["roofline"]["clock_source"] = prof["clock_source"]
+    result["roofline"] = r.pop("roofline")
+    for key in ("value", "ms_per_step"):
+        r.pop(key)
+    result.update(r)
+    if not args.no_workloads and args.workload == "64k":
+        result["workloads"] = {}
+        for name in ("8k", "varlen", "256k"):
+            steps = 3 if name == "256k" else 10
+            log("workload %s (%d steps) ..." % (name, steps))
+            wr = measure_workload(uly, torch, workloads.WORKLOADS[name], steps, 2, swaps_alone=False)
+            result["workloads"][name] = {
+                "config": wr["config"]["workload"], "steps": steps, "ms_per_step": wr["ms_per_step"],
+                "value_tflops": wr["value"], "attn_tflops": wr["attn_tflops"], "attn_frac_peak": wr["attn_frac_peak"],
+                "kernel_ms": wr["kernel_ms"], "kernel_tflops": wr["kernel_tflops"],
+                "swap_gbps": wr["swap_gbps"], "roofline": wr["roofline"],
+            }
     if not args.no_ring and cu is None:
-        log("ring attention step (rank %d of %d) ..." % (P - 1, P))
-        result["ring"] = ring_step(uly, torch, w, x_seq, dy_seq)
+        log("ring attention step (rank %d of %d) ..." % (w.P - 1, w.P))
+        result["ring"] = ring_step(uly, torch, w)
     if not args.no_loss:
         log("shifted-label loss (%d tokens x %d vocab) ..." % (w.n, 151936))
         result["loss"] = loss_step(uly, torch, w)

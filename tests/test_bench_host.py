@@ -65,12 +65,21 @@ def test_traffic_summary_calibrates_on_the_pack_and_tracks_the_sources(bench, tm
     pmc.mkdir()
     _write_counters(pmc / "fetch_counter_collection.csv", "FETCH_SIZE", [(1, pack, shard / 2 / 1024), (2, dkdv, 1000.0)])
     _write_counters(pmc / "write_counter_collection.csv", "WRITE_SIZE", [(1, pack, shard / 1024), (2, dkdv, 300.0)])
+    # the clock pass: GRBM_GUI_ACTIVE summed over 8 XCDs, with the kernel trace of the same run
+    _write_counters(pmc / "grbm_counter_collection.csv", "GRBM_GUI_ACTIVE",
+                    [(1, pack, 8 * 2.0 * 50_000), (2, dkdv, 8 * 1.9 * 17_000_000)])
+    with open(pmc / "grbm_kernel_trace.csv", "w", newline="") as fh:
+        wr = csv.DictWriter(fh, fieldnames=["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        wr.writeheader()
+        wr.writerow({"Dispatch_Id": 1, "Kernel_Name": pack, "Start_Timestamp": 1000, "End_Timestamp": 51_000})
+        wr.writerow({"Dispatch_Id": 2, "Kernel_Name": dkdv, "Start_Timestamp": 60_000, "End_Timestamp": 17_060_000})
     bench.write_traffic_summary("64k", str(pmc))
-    got = bench.measured_traffic("64k", "a8_attn_bwd_dkdv")
-    assert got == int(round((1000.0 * 2.0 + 300.0 * 1.0) * 1024))
-    assert bench.measured_traffic("64k", "a3_attn_fwd") is None          # no such dispatch
+    got = bench.measured_profile("64k", "a8_attn_bwd_dkdv")
+    assert got["hbm_bytes"] == int(round((1000.0 * 2.0 + 300.0 * 1.0) * 1024))
+    assert abs(got["clock_ghz"] - 1.9) < 1e-9
+    assert bench.measured_profile("64k", "a3_attn_fwd") is None          # no such dispatch
     (root / "long_context_attention_ulysses_amd" / "csrc" / "k.hip").write_text("// v2\n")
-    assert bench.measured_traffic("64k", "a8_attn_bwd_dkdv") is None     # kernels changed since
+    assert bench.measured_profile("64k", "a8_attn_bwd_dkdv") is None     # kernels changed since
 
 
 def test_bench_refuses_more_than_one_gpu(bench, monkeypatch, capsys):
