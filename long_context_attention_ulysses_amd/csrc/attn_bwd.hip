@@ -42,6 +42,14 @@
 #ifndef ULY_TR_LA
 #define ULY_TR_LA 4
 #endif
+// Read-ahead hint for the dq kernel's transposing reads (0: none).
+#ifndef ULY_DQ_HINT
+#define ULY_DQ_HINT 0
+#endif
+// 16-query steps of the deferred dK update done in phase 1 (the rest in phase 2).
+#ifndef ULY_DK_P1
+#define ULY_DK_P1 4
+#endif
 
 namespace uly {
 
@@ -71,6 +79,10 @@ struct BwdArgs {
 
 // ------------------------------------------------------------ dq kernel ----
 
+// kTr (d = 128): the K^T operand of dQ^T += K^T dS^T is read transposed
+// from the K row tile (rt2 layout, as in the dK/dV kernel) instead of being
+// copied from the transposed copy of K, so each key tile copies K and V rows
+// only.
 template <int D, int HPW, int RB>
 struct DqCfg {
   static constexpr int NW = HPW * RB;
@@ -83,15 +95,18 @@ struct DqCfg {
   static constexpr int TILE = BN * D;
   static constexpr int NI = TILE / 512;    // 1 KiB copies per tile and tensor
   static_assert(NI % NW == 0, "copies must split evenly over the waves");
-  static constexpr int NLW = 3 * NI / NW;  // copies per wave per tile (K, V, K^T)
+  static constexpr bool kTr = D == 128;
+  static constexpr int NLW = (kTr ? 2 : 3) * NI / NW;  // copies per wave per tile (K, V[, K^T])
 };
 
 template <int D, int HPW, int RB, bool kSplit>
 __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_bwd_dq_kernel(BwdArgs a) {
   using C = DqCfg<D, HPW, RB>;
+  constexpr bool kTr = C::kTr;
+  constexpr int TT = kTr ? 8 : C::TILE;  // trans tiles (unused with kTr)
   __shared__ __align__(16) bf16_t k0[C::TILE], k1[C::TILE], k2[C::TILE];
   __shared__ __align__(16) bf16_t v0[C::TILE], v1[C::TILE], v2[C::TILE];
-  __shared__ __align__(16) bf16_t t0_[C::TILE], t1_[C::TILE], t2_[C::TILE];
+  __shared__ __align__(16) bf16_t t0_[TT], t1_[TT], t2_[TT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -172,17 +187,27 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_bwd_dq_kernel(BwdArgs a
   const bf16_t *kbase = a.k + (int64_t)g * D, *vbase = a.v + (int64_t)g * D;
   const uint32_t kbytes = head_rows_bytes(a.N, a.k_stride, D), vbytes = head_rows_bytes(a.N, a.v_stride, D);
   const BufRes trs = make_rsrc(a.kt + (int64_t)g * D * a.Np, (uint32_t)(D * a.Np * 2));
+  // Row-tile layout of the K and V tiles (rt2 with kTr: K is also read transposed).
+  auto roff = [](int r, int c) __attribute__((always_inline)) {
+    if constexpr (kTr) return rt2_off(r, c);
+    else return rt_off<D>(r, c);
+  };
+  auto rswz = [](int r) __attribute__((always_inline)) {
+    if constexpr (kTr) return rt2_swz(r);
+    else return row_swz<D>(r);
+  };
   uint32_t koff[C::NI / C::NW], voff[C::NI / C::NW], toff[C::NI / C::NW];
 #pragma unroll
   for (int i = 0; i < C::NI / C::NW; ++i) {
     const int s = (w + i * C::NW) * 64 + lane;
     const int r = s / (D / 8);
-    const uint32_t cb = ((s % (D / 8)) ^ row_swz<D>(r)) << 4;
+    const uint32_t cb = ((s % (D / 8)) ^ rswz(r)) << 4;
     koff[i] = r * ksb + cb;
     voff[i] = r * vsb + cb;
     const int d = s >> 3;
     toff[i] = (uint32_t)(d * a.Np * 2) + (((s & 7) ^ ((d >> 1) & 7)) << 4);
   }
+  [[maybe_unused]] const TrOffsets tro = kTr ? tr_offsets(lane) : TrOffsets{};
 
   // K and V rows from tile row t0 on (resources from row t0 to the end of
   // row N-1).
@@ -195,7 +220,7 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_bwd_dq_kernel(BwdArgs a
       const int u = w + i * C::NW;
       dma16(krs, koff[i], 0, ks_ + u * 512);
       dma16(vrs, voff[i], 0, vs_ + u * 512);
-      dma16(trs, toff[i], t0 * 2, ts_ + u * 512);
+      if constexpr (!kTr) dma16(trs, toff[i], t0 * 2, ts_ + u * 512);
     }
   };
 
@@ -215,7 +240,7 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_bwd_dq_kernel(BwdArgs a
       }
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
-        const int off = rt_off<D>(kb * 32 + l32, ks * 2 + hi32);
+        const int off = roff(kb * 32 + l32, ks * 2 + hi32);
         const bf16x8 ak = as_bf16x8(*reinterpret_cast<const u32x4 *>(ks_ + off));
         const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4 *>(vs_ + off));
         s = mfma32(ak, qf[ks], s);
@@ -240,11 +265,15 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_bwd_dq_kernel(BwdArgs a
         const bf16x8 dsf = cvt8(s[b + 0], s[b + 1], s[b + 2], s[b + 3], s[b + 4], s[b + 5], s[b + 6], s[b + 7]);
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-          const bf16x8 ak =
-              as_bf16x8(*reinterpret_cast<const u32x4 *>(ts_ + tr_off(db * 32 + l32, 2 * j + hi32)));
+          bf16x8 ak;
+          if constexpr (kTr) ak = tr_frag(lds_addr(ks_), tro, db, j);
+          else ak = as_bf16x8(*reinterpret_cast<const u32x4 *>(ts_ + tr_off(db * 32 + l32, 2 * j + hi32)));
           acc[db] = mfma32(ak, dsf, acc[db]);
         }
       }
+#if ULY_DQ_HINT
+      if constexpr (kTr) pipeline_reads_mfma_n<2 * C::DB, 2, 2>();
+#endif
     }
   };
 
@@ -533,10 +562,12 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
 
     // dK^T += Q^T(t-1) dS(t-1): Q^T from its trans tile, or (kTr) read
     // transposed from tile t-1's Q rows.
-    auto dk_update = [&](const bf16_t *qts) __attribute__((always_inline)) {
+    // Query steps [C0, C1) of the update.
+    auto dk_update = [&](const bf16_t *qts, auto c0, auto c1) __attribute__((always_inline)) {
+      constexpr int C0 = decltype(c0)::value, C1 = decltype(c1)::value;
       [[maybe_unused]] const uint32_t qa = lds_addr(qts);
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+      for (int c = C0; c < C1; ++c)
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
           bf16x8 aqt;
@@ -544,9 +575,12 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
           else aqt = as_bf16x8(*reinterpret_cast<const u32x4 *>(qts + tr_off(db * 32 + l32, c * 2 + hi32)));
           acc[db] = mfma32(aqt, sf[c], acc[db]);
         }
-      if constexpr (kTr) pipeline_reads_mfma_n<4 * C::DB, 2, ULY_TR_LA>();
-      else pipeline_reads_mfma<4 * C::DB>();
+      if constexpr (kTr) pipeline_reads_mfma_n<(C1 - C0) * C::DB, 2, ULY_TR_LA>();
+      else pipeline_reads_mfma<(C1 - C0) * C::DB>();
     };
+    using IC0 = std::integral_constant<int, 0>;
+    using ICP1 = std::integral_constant<int, kTr ? ULY_DK_P1 : 4>;
+    using IC4 = std::integral_constant<int, 4>;
 
     // qs_prev: Q^T(t-1) trans tile, or (kTr) tile t-1's Q rows.
     // qs_n, ds_n, ls_n: stages for tile t + PF's copies.
@@ -572,7 +606,7 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
       f32x16 x[2];
       bf16x8 pf[4];
       if constexpr (!S) {
-        if (pend) dk_update(qs_prev);
+        if (pend) dk_update(qs_prev, IC0{}, ICP1{});
       }
       if (act) {
 #pragma unroll
@@ -638,6 +672,9 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
           else pipeline_reads_mfma<4 * C::DB>();
         }
       } else {
+        if constexpr (ICP1::value < 4) {
+          if (pend) dk_update(qs_prev, ICP1{}, IC4{});
+        }
         pend = act;
         if (act) {
 #pragma unroll
@@ -678,7 +715,7 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
       }
       // The last tile's dK update (its Q rows stay in place: nothing more is copied).
       if constexpr (!S) {
-        if (pend) dk_update(qrow[(te - 1 - tb) % QST]);
+        if (pend) dk_update(qrow[(te - 1 - tb) % QST], IC0{}, IC4{});
       }
     } else {
       if (tb < te) {
@@ -694,7 +731,7 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
       wait_vmcnt<0>();
       barrier();
       if constexpr (!S) {
-        if (pend) dk_update((te - 1 - tb) % 2 == 0 ? qtt[0] : qtt[1]);
+        if (pend) dk_update((te - 1 - tb) % 2 == 0 ? qtt[0] : qtt[1], IC0{}, IC4{});
       }
     }
   };
@@ -953,8 +990,8 @@ int launch_attn_bwd(const AttnShape &s, const AttnBwdPtrs &p, int parts, hipStre
     bf16_t *ws_kt = reinterpret_cast<bf16_t *>(p.ws + L.kt);
     bf16_t *ws_qt = reinterpret_cast<bf16_t *>(p.ws + L.qt);
     bf16_t *ws_dot = reinterpret_cast<bf16_t *>(p.ws + L.dot);
-    if ((rc = launch_to_trans(p.k, s.k_stride, s.hkv, s.d, s.N, ws_kt, stream))) return rc;
-    if (s.d != 128) {  // at d = 128 the dK/dV kernel reads Q and dO rows transposed in LDS
+    if (s.d != 128) {  // at d = 128 both kernels read the row tiles transposed in LDS
+      if ((rc = launch_to_trans(p.k, s.k_stride, s.hkv, s.d, s.N, ws_kt, stream))) return rc;
       if ((rc = launch_to_trans(p.q, s.q_stride, s.hq, s.d, s.N, ws_qt, stream))) return rc;
       if ((rc = launch_to_trans(p.dout, p.do_stride, s.hq, s.d, s.N, ws_dot, stream))) return rc;
     }
