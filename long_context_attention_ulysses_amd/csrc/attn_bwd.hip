@@ -912,12 +912,12 @@ int launch_dkdv_cfg(BwdArgs a, hipStream_t stream) {
     if (rc) return rc;
   }
   constexpr bool kTr = D == 128;
-  if (a.ksplit > 1)
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true, kTr>), dim3((unsigned)((int64_t)a.nblk * a.hkv * a.ksplit)),
-                       dim3(C::NT), 0, stream, a);
-  else
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false, kTr>), dim3((unsigned)((int64_t)a.nblk * a.hkv)),
-                       dim3(C::NT), 0, stream, a);
+  const unsigned grid = (unsigned)((int64_t)a.nblk * a.hkv * a.ksplit);
+  if (a.ksplit > 1) {
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true, kTr>), dim3(grid), dim3(C::NT), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false, kTr>), dim3(grid), dim3(C::NT), 0, stream, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_hip_error(e, "attn_bwd_dkdv_kernel");
   if (a.ksplit > 1) {
