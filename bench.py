@@ -458,7 +458,7 @@ def csrc_digest():
 
 def measured_profile(workload: str, step_name: str):
     """What the committed rocprofv3 counter summary (profiles/traffic_<workload>.txt)
-    says about a kernel's first dispatch in the profiled step: HBM bytes
+    says about a kernel's last dispatch in the profiled steps: HBM bytes
     (FETCH_SIZE + WRITE_SIZE, scaled by the readings of a copy of known size)
     and the engine clock (GRBM_GUI_ACTIVE cycles over the 8 XCDs / the
     dispatch's duration). None when there is no summary for this workload or
@@ -471,13 +471,13 @@ def measured_profile(workload: str, step_name: str):
     if doc.get("source_sha256") != csrc_digest():
         return None
     prefix = KERNEL_OF[step_name]
-    # the first dispatch of the kernel is the one in the profiled step
+    # the kernel's last dispatch: the last profiled step (after a warm-up step)
     hits = [d for d in doc["dispatches"] if d["kernel"].startswith(prefix)]
     if not hits:
         return None
-    out = {"hbm_bytes": hits[0]["hbm_bytes"]}
-    if hits[0].get("clock_ghz"):
-        out["clock_ghz"] = hits[0]["clock_ghz"]
+    out = {"hbm_bytes": hits[-1]["hbm_bytes"]}
+    if hits[-1].get("clock_ghz"):
+        out["clock_ghz"] = hits[-1]["clock_ghz"]
         out["clock_source"] = ("GRBM_GUI_ACTIVE / 8 XCDs / kernel duration of the same dispatch "
                                "(profiles/traffic_%s.txt)" % workload)
     return out
@@ -491,7 +491,7 @@ def short_kernel_name(full: str) -> str:
 
 
 def write_traffic_summary(workload: str, pmc_dir: str):
-    """Turn the rocprofv3 counter runs of `bench.py --steps 1 --warmup 0`
+    """Turn the rocprofv3 counter runs of `bench.py --steps 2 --warmup 1`
     into profiles/traffic_<workload>.txt:
       - FETCH_SIZE in <pmc_dir>/fetch_counter_collection.csv and WRITE_SIZE in
         <pmc_dir>/write_counter_collection.csv: HBM bytes per dispatch. Both
@@ -534,10 +534,10 @@ def write_traffic_summary(workload: str, pmc_dir: str):
     assert fetch[0][1].startswith("swap"), fetch[0][1]
     fetch_scale = shard_bytes / (fetch[0][2] * 1024)
     write_scale = shard_bytes / (write[0][2] * 1024)
-    run = ("-- python3 $REPO/bench.py --workload %s --steps 1 --warmup 0 --cpu-tokens 0 --no-ring --no-loss "
+    run = ("-- python3 $REPO/bench.py --workload %s --steps 2 --warmup 1 --cpu-tokens 0 --no-ring --no-loss "
            "--no-mlp --no-workloads" % workload)
     doc = {
-        "workload": "%s head shard, one bench step (--steps 1 --warmup 0)" % workload,
+        "workload": "%s head shard, one warm-up and two timed bench steps (--steps 2 --warmup 1)" % workload,
         "commands": [
             "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $PMC -o fetch " + run,
             "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $PMC -o write " + run,
