@@ -101,7 +101,8 @@ int ulysses_check_cu_seqlens(const int32_t *cu, int32_t n_seqs, int64_t N);
  *            (the head count must divide by the SP degree: "Ulysses sequence
  *            parallelism", Configure, the warning on attention heads).
  * d: head dim, a multiple of 8 (any such value, not only 64/128).
- * Errors: ULY_E_NULL, ULY_E_SHAPE (n_local, P, d, n_seg out of range),
+ * Errors: ULY_E_NULL, ULY_E_SHAPE (n_local, P, d, n_seg out of range, or a
+ * tensor of 2^31 16-byte vectors or more: n_local*H*d >= 2^34),
  * ULY_E_DIV_P, ULY_E_ALIGN, ULY_E_ALIAS (x_seq and x_send overlap), ULY_E_HIP.
  * Receiving a chunk from every rank in rank order gives the head shard
  * [N][H/P][d] with tokens in sequence order (intro diagram: GPU 0 holds the

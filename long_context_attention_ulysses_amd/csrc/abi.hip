@@ -62,7 +62,6 @@ int check_swap(const void *src, const void *dst, int64_t n, int32_t P, int32_t n
   }
   // every 16-byte vector index of the tensor must fit the kernels' 32-bit indexes
   if (n * H * d / 8 >= (int64_t)1 << 31) return ULY_E_SHAPE;
-  if (P * nseg > 1 << 16) return ULY_E_SHAPE;
   if (!aligned16(src) || !aligned16(dst)) return ULY_E_ALIGN;
   const size_t bytes = (size_t)(n * H * d * 2);
   if (overlaps(src, bytes, dst, bytes)) return ULY_E_ALIAS;

@@ -8,9 +8,6 @@
 
 namespace uly {
 
-// (chunk, segment) runs handled by one swap launch (grid.y).
-constexpr int kMaxSwapRuns = 32;
-
 // Records a HIP error message for uly_last_error() and returns ULY_E_HIP.
 int set_hip_error(hipError_t e, const char *where);
 

@@ -58,7 +58,7 @@ def test_traffic_summary_calibrates_on_the_pack_and_tracks_the_sources(bench, tm
     monkeypatch.setattr(bench, "ROOT", str(root))
     w = workloads.WORKLOADS["64k"]
     shard = w.n * w.Ht * w.d * 2
-    pack = "void uly::(anonymous namespace)::swap_rows_kernel<true>(uly::(anonymous namespace)::RowArgs)"
+    pack = "void uly::(anonymous namespace)::swap_kernel<true>(uly::(anonymous namespace)::SwapArgs)"
     dkdv = "void uly::(anonymous namespace)::attn_bwd_dkdv_kernel<128, false>(uly::(anonymous namespace)::BwdArgs)"
     # counters in KiB; FETCH_SIZE reads half the true bytes on the pack, WRITE_SIZE all of them
     pmc = tmp_path / "pmc"
