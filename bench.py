@@ -87,38 +87,59 @@ KERNEL_OF = {"a3_attn_fwd": "attn_fwd_kernel", "a7a9_attn_bwd_dq": "attn_bwd_dq_
              "a8_attn_bwd_dkdv": "attn_bwd_dkdv_kernel"}
 
 
-def swap_cold_warm(torch, fns, reps=10):
-    """Each swap timed alone, outside the step: cold (a 512 MiB scratch write
-    between repetitions evicts the MALL) and warm (back to back), medians of
-    `reps`, each beside a device-to-device copy of the same bytes as the
-    achievable-copy reference. Bytes counted: one read + one write.
+def swap_cold_warm(torch, fns, reps=15, batch=20):
+    """Each swap timed alone, outside the step, cold and warm, beside a
+    device-to-device copy of the same bytes as the achievable-copy reference.
+    Bytes counted: one read + one write.
+
+    An event recorded right before a kernel holds that kernel back by about
+    6 us (the marker's own completion), and after a synchronization the first
+    event fires before the host has submitted the launch. So neither timing
+    puts an event directly in front of the kernel it measures:
+      warm: `batch` launches back to back between two events, per launch;
+      cold: [MALL-evicting 512 MiB scratch write, then the swap] minus [the
+            same scratch write alone], both between two events, medians of
+            `reps` alternating pairs.
     fns: {name: (launch, src, dst)} with src/dst the swap's tensors."""
     import numpy as np
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
 
-    def timed(fn, nbytes, cold):
-        ts = []
-        for _ in range(reps):
-            if cold:
-                scratch.fill_(1)
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            fn()
-            e1.record()
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        ms = float(np.median(ts))
+    def between(*calls):
+        torch.cuda.synchronize()
+        e0.record()
+        for c in calls:
+            c()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    evict = lambda: scratch.fill_(1)  # noqa: E731
+
+    def rate(ms, nbytes):
         return {"ms": round(ms, 4), "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
                 "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+    def timed_cold(fn, nbytes):
+        with_fn, alone = [], []
+        for _ in range(reps):
+            with_fn.append(between(evict, fn))
+            alone.append(between(evict))
+        return rate(float(np.median(with_fn)) - float(np.median(alone)), nbytes)
+
+    def timed_warm(fn, nbytes):
+        fn()
+        ts = [between(*([fn] * batch)) / batch for _ in range(max(3, reps // 5))]
+        return rate(float(np.median(ts)), nbytes)
 
     out = {}
     for name, (launch, src, dst) in fns.items():
         nbytes = 2 * src.numel() * src.element_size()
         flat_src, flat_dst = src.reshape(-1), dst.view(-1)
         copy = lambda: flat_dst.copy_(flat_src)  # noqa: E731
-        out[name] = {"bytes": nbytes, "cold": timed(launch, nbytes, True), "warm": timed(launch, nbytes, False),
-                     "d2d_copy_cold": timed(copy, nbytes, True), "d2d_copy_warm": timed(copy, nbytes, False)}
+        out[name] = {"bytes": nbytes, "cold": timed_cold(launch, nbytes), "warm": timed_warm(launch, nbytes),
+                     "d2d_copy_cold": timed_cold(copy, nbytes), "d2d_copy_warm": timed_warm(copy, nbytes)}
     del scratch
     return out
 
@@ -364,27 +385,46 @@ def measure_workload(uly, torch, w, steps, warmup, swaps_alone):
     total_flops = 14.0 * d * U * hq
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+    # The dK/dV kernel carries 8 of the 14 counted d-units per pair, so it
+    # is the dominant kernel of every workload; the timed steps bracket only
+    # it with events.
+    DOM = names.index("a8_attn_bwd_dkdv")
+    dom_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
 
-    def step(ev=None):
+    def step(ev=None, dom_ev=None):
         if ev is not None:
             ev[0].record()
         for i, f in enumerate(launches):
+            if dom_ev is not None and i == DOM:
+                dom_ev[0].record()
             f()
             if ev is not None:
                 ev[i + 1].record()
+            if dom_ev is not None and i == DOM:
+                dom_ev[1].record()
 
     for i in range(warmup):
         step()
         torch.cuda.synchronize()
         log("warmup step %d done" % (i + 1))
+    # An event recorded between two kernels holds the second one back by
+    # about 6 us, so the timed steps record events only around the dominant
+    # kernel; the per-kernel breakdown comes from a second pass of the same
+    # number of steps with an event after every launch.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(events[i])
+        step(dom_ev=dom_events[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / steps
     log("timed %d steps: %.3f ms/step" % (steps, ms_per_step))
+    t2 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    ms_per_step_events = (time.perf_counter() - t2) * 1e3 / steps
+    log("breakdown pass: %.3f ms/step with an event after every launch" % ms_per_step_events)
 
     kern_all = {nm: [events[s_][i].elapsed_time(events[s_][i + 1]) for s_ in range(steps)]
                 for i, nm in enumerate(names)}
@@ -392,12 +432,14 @@ def measure_workload(uly, torch, w, steps, warmup, swaps_alone):
     kern_med = {nm: float(np.median(v_)) for nm, v_ in kern_all.items()}
     attn_ms = kern_ms["a3_attn_fwd"] + kern_ms["a7a9_attn_bwd_dq"] + kern_ms["a8_attn_bwd_dkdv"]
     swap_gbps = {nm: swap_bytes[nm] / (kern_ms[nm] * 1e-3) / 1e9 for nm in swap_bytes}
-    dom = max(flops, key=lambda nm: kern_ms[nm])
-    achieved = flops[dom] / (kern_ms[dom] * 1e-3) / 1e12
+    dom = names[DOM]
+    dom_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in dom_events]))
+    achieved = flops[dom] / (dom_ms * 1e-3) / 1e12
     value = total_flops / (ms_per_step * 1e-3) / 1e12
 
     roofline = {
         "kernel": dom,
+        "launch_ms": round(dom_ms, 4),   # HIP events around each of its launches in the timed steps
         "bound": "mfma",
         "achieved": round(achieved, 2),
         "peak": BF16_PEAK_TFLOPS,
@@ -408,6 +450,7 @@ def measure_workload(uly, torch, w, steps, warmup, swaps_alone):
     out = {
         "value": round(value, 3),
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_with_events": round(ms_per_step_events, 4),
         "config": {
             "workload": "Qwen3-4B-shaped SP=%d head shard, %s: N=%d tokens, %d q / %d kv heads, d=%d, causal%s"
                         % (P, w.name, w.N, hq, hkv, d, ", packed docs" if cu is not None else ""),
@@ -425,8 +468,9 @@ def measure_workload(uly, torch, w, steps, warmup, swaps_alone):
         "fwd_tflops": round(4.0 * d * U * hq / (kern_ms["a3_attn_fwd"] * 1e-3) / 1e12, 2),
         "bwd_tflops": round(10.0 * d * U * hq / ((kern_ms["a7a9_attn_bwd_dq"] + kern_ms["a8_attn_bwd_dkdv"]) * 1e-3)
                             / 1e12, 2),
-        "swap_gbps": {k_: round(v_, 1) for k_, v_ in swap_gbps.items()},
-        "swap_frac_hbm": {k_: round(v_ / HBM_PEAK_GBPS, 4) for k_, v_ in swap_gbps.items()},
+        # from the breakdown pass: each includes the ~6 us by which the event
+        # recorded in front of it holds it back
+        "swap_gbps_breakdown": {k_: round(v_, 1) for k_, v_ in swap_gbps.items()},
         "counted_flop_per_step": total_flops,
         "peak_device_bytes": torch.cuda.max_memory_allocated(),
         "unmasked_pairs_per_head": U,
@@ -438,6 +482,10 @@ def measure_workload(uly, torch, w, steps, warmup, swaps_alone):
             "a6_pack_do": (launches[3], dy_seq, dsend),
             "a10_unpack_dqkv": (launches[6], g_chunks, dqkv_seq),
         })
+        # The swaps' rates: each alone and cold (timed without an event in
+        # front of it; they agree with the kernel trace's durations).
+        out["swap_gbps"] = {k_: v_["cold"]["gbps"] for k_, v_ in out["swaps_alone"].items()}
+        out["swap_frac_hbm"] = {k_: v_["cold"]["frac_hbm"] for k_, v_ in out["swaps_alone"].items()}
     del x_seq, recv, dy_seq, dy_head, send, o, lse, o_seq, dsend, dqkv, dqkv_seq, ws, ws_fwd
     torch.cuda.empty_cache()
     return out
@@ -641,7 +689,7 @@ def main():
                 "config": wr["config"]["workload"], "steps": steps, "ms_per_step": wr["ms_per_step"],
                 "value_tflops": wr["value"], "attn_tflops": wr["attn_tflops"], "attn_frac_peak": wr["attn_frac_peak"],
                 "kernel_ms": wr["kernel_ms"], "kernel_tflops": wr["kernel_tflops"],
-                "swap_gbps": wr["swap_gbps"], "roofline": wr["roofline"],
+                "swap_gbps_breakdown": wr["swap_gbps_breakdown"], "roofline": wr["roofline"],
             }
     if not args.no_ring and cu is None:
         log("ring attention step (rank %d of %d) ..." % (w.P - 1, w.P))
