@@ -156,8 +156,8 @@ int attn_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *
  * is a static buffer of ULY_NOALLOC_SCRATCH_BYTES (80 MiB) that the library
  * holds on every GPU it runs on until the process ends. Problems whose
  * attn_fwd_workspace_bytes(N, hq, hkv, d) exceed that return ULY_E_SCRATCH
- * (before anything is launched). At d = 128 that allows up to 327,680
- * tokens with one KV head or 163,840 with two; every head shard of the
+ * (before anything is launched). At d = 128 that allows up to 327,552
+ * tokens with one KV head or 163,776 with two; every head shard of the
  * 8K, 64K, packed 64K and 256K workloads fits.
  * The device is the stream's (the current device for stream 0). The first
  * call on a device looks up the buffer's address there; that lookup can
@@ -175,7 +175,9 @@ int attn_fwd_noalloc(const uint16_t *q, const uint16_t *k, const uint16_t *v, ui
  * 512 (query block of 256 / hpw rows, group of hpw query heads) pairs, hpw
  * the largest of 4, 2, 1 dividing hq / hkv, s * N * hq * (d + 2) * 4 bytes
  * more, s = min(4, ceil(512 / pairs)), rounded up to 256: float32 partial
- * softmax states of the s workgroups that then share each pair's keys. */
+ * softmax states of the s workgroups that then share each pair's keys; then
+ * roundup(N, 64) / 64 int32 entries, rounded up to 256 bytes (the order of
+ * the query blocks over packed documents). */
 size_t attn_fwd_workspace_bytes(int64_t N, int32_t hq, int32_t hkv, int32_t d);
 
 /*
@@ -201,9 +203,10 @@ int attn_fwd_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v, uin
 
 /* Workspace the backward pass needs: float32 D = rowsum(dO * O) and
  * LSE*log2(e), [hq][roundup(N, 64)] each, then transposed copies of K, Q and
- * dO (hkv, hq and hq heads of d * roundup(N, 64) bf16), then an int32 array
- * of roundup(N, 64) / 64 entries (the varlen workgroup order of the dK/dV
- * pass), and, when there are fewer than 512 (128-key block, KV head) pairs,
+ * dO (hkv, hq and hq heads of d * roundup(N, 64) bf16), then two int32
+ * arrays of roundup(N, 64) / 64 entries (the workgroup orders of the dK/dV
+ * and dq passes over packed documents), and, when there are fewer than 512
+ * (128-key block, KV head) pairs,
  * float32 partial dK/dV of s * N * hkv * 2 * d values, s = min(4,
  * ceil(512 / pairs)) (the dK/dV pass then splits each pair's queries over s
  * workgroups), and, when there are fewer than 512 (query block of 256 / hpw
@@ -259,12 +262,13 @@ int attn_bwd_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
  * Long Sequence Training"): dq sums over keys, dk and dv over queries, so
  * each step is one pass that recomputes the scores it needs.
  *
- * attn_bwd_dq: fills ws (D, LSE*log2(e), the transposed copies of K and,
- *   at d = 64, of Q and dO) and writes dq.
- * attn_bwd_dkdv: dk and dv. It reads D, LSE*log2(e) and (d = 64) the
- *   transposed copies of Q and dO from ws as left by attn_bwd_dq with the same
- *   arguments (not to be modified in between), and writes two other regions
- *   of ws: the order of its key blocks (packed documents) and its float32
+ * attn_bwd_dq: fills ws (D, LSE*log2(e), at d = 64 the transposed copies of
+ *   K, Q and dO, over packed documents the block orders of both steps) and
+ *   writes dq.
+ * attn_bwd_dkdv: dk and dv. It reads D, LSE*log2(e), (d = 64) the
+ *   transposed copies of Q and dO and (packed documents) its key-block order
+ *   from ws as left by attn_bwd_dq with the same arguments (not to be
+ *   modified in between), and writes another region of ws: its float32
  *   partial dK/dV (when it splits its query ranges, see
  *   attn_bwd_workspace_bytes). Calls that may run at the same time therefore
  *   need workspaces of their own.

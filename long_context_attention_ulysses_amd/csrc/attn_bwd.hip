@@ -26,8 +26,8 @@
 //      P, dS, dV^T += dO^T P, dK^T += Q^T dS.
 // Small problems (fewer than 512 blocks of either kernel) split each block's
 // tiles over up to 4 workgroups that write float32 partials, summed in split
-// order by a second pass (still deterministic); over packed documents the
-// dkdv kernel takes its key blocks in order of decreasing work.
+// order by a second pass (still deterministic); over packed documents both
+// kernels take their blocks in order of decreasing work.
 #include <type_traits>
 
 #include "attn_common.h"
@@ -71,6 +71,7 @@ struct BwdArgs {
   const int32_t *cu;
   int n_seqs;
   const int32_t *korder;  // packed documents: key blocks by decreasing work
+  const int32_t *qorder;  // packed documents: dq query blocks by decreasing work
   int ksplit;             // dK/dV: workgroups per (key block, KV head)
   float *dkv_part;        // dK/dV partials [ksplit][N][hkv][2][d] when ksplit > 1
   int qsplit;             // dq: workgroups per (query block, head group)
@@ -117,7 +118,8 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_bwd_dq_kernel(BwdArgs a
   // With a split the pieces of one query block are consecutive ids.
   const int item = blockIdx.x;
   const int hg = item % a.nhg;
-  const int qb = a.nblk - 1 - (kSplit ? item / a.nhg / a.qsplit : item / a.nhg);
+  const int qbi = kSplit ? item / a.nhg / a.qsplit : item / a.nhg;
+  const int qb = a.qorder ? a.qorder[qbi] : a.nblk - 1 - qbi;
   const int split = kSplit ? item / a.nhg % a.qsplit : 0;
   const int64_t q0 = (int64_t)qb * C::BM;
   const int h = hg * HPW + w / RB;
@@ -808,68 +810,6 @@ __global__ void __launch_bounds__(256) dkdv_part_sum_kernel(PartSumArgs a) {
   *reinterpret_cast<u32x4 *>(dst + (int64_t)g * a.d + c * 8) = o;
 }
 
-// Key-block schedule of the dK/dV kernel over packed documents (one
-// workgroup): the work of every block of bs keys is the number of 64-query
-// tiles its query range spans (the kernel's own ranges), then a bitonic sort
-// in LDS of (work, id) keys, so the longest blocks start first. Without it
-// the blocks go in key order, which under the causal mask is heaviest-first
-// only within one document; at 64K with documents of 512-8192 tokens the
-// sort took the kernel from 2.15 to 1.70-1.78 ms. More than kMaxOrder blocks
-// keep the key order.
-constexpr int kOrderThreads = 1024;
-constexpr int kMaxOrder = 16384;
-
-__global__ void __launch_bounds__(kOrderThreads) key_block_order_kernel(const int32_t *cu, int n_seqs,
-                                                                        int64_t N, int causal, int bs, int nb,
-                                                                        int32_t *order) {
-  __shared__ uint64_t keys[kMaxOrder];
-  const int tid = threadIdx.x;
-  if (nb > kMaxOrder) {
-    for (int i = tid; i < nb; i += kOrderThreads) order[i] = i;
-    return;
-  }
-  int p2 = 1;
-  while (p2 < nb) p2 <<= 1;
-  for (int i = tid; i < p2; i += kOrderThreads) {
-    uint64_t key = ~0ull;
-    if (i < nb) {
-      const int64_t b0 = (int64_t)i * bs;
-      const int64_t b1 = (b0 + bs < N ? b0 + bs : N) - 1;
-      const int64_t lo = query_range(cu, n_seqs, N, causal, b0).lo;
-      const int64_t hi = query_range(cu, n_seqs, N, causal, b1).hi;
-      const uint32_t work = (uint32_t)((hi + 63) / 64 - lo / 64);
-      key = ((uint64_t)(0xFFFFFFFFu - work) << 32) | (uint32_t)i;
-    }
-    keys[i] = key;
-  }
-  __syncthreads();
-  for (int k = 2; k <= p2; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < p2; i += kOrderThreads) {
-        const int l = i ^ j;
-        if (l > i) {
-          const uint64_t x = keys[i], y = keys[l];
-          if ((x > y) == ((i & k) == 0)) {
-            keys[i] = y;
-            keys[l] = x;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
-  for (int i = tid; i < nb; i += kOrderThreads) order[i] = (int32_t)(uint32_t)keys[i];
-}
-
-int launch_key_block_order(const int32_t *cu, int n_seqs, int64_t N, int causal, int bs, int nb,
-                           int32_t *order, hipStream_t stream) {
-  hipLaunchKernelGGL(key_block_order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, cu, n_seqs, N, causal, bs,
-                     nb, order);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return set_hip_error(e, "key_block_order_kernel");
-  return 0;
-}
-
 template <int D, int HPW, int RB>
 int launch_dq_cfg(BwdArgs a, hipStream_t stream) {
   using C = DqCfg<D, HPW, RB>;
@@ -906,11 +846,6 @@ int launch_dkdv_cfg(BwdArgs a, hipStream_t stream) {
   using C = DkvCfg<D>;
   a.nblk = (int)((a.N + C::BNK - 1) / C::BNK);
   a.ksplit = dkdv_ksplit(a.N, a.hkv);
-  if (a.korder) {
-    const int rc = launch_key_block_order(a.cu, a.n_seqs, a.N, a.causal, C::BNK, a.nblk,
-                                          const_cast<int32_t *>(a.korder), stream);
-    if (rc) return rc;
-  }
   constexpr bool kTr = D == 128;
   const unsigned grid = (unsigned)((int64_t)a.nblk * a.hkv * a.ksplit);
   if (a.ksplit > 1) {
@@ -978,6 +913,7 @@ int launch_attn_bwd(const AttnShape &s, const AttnBwdPtrs &p, int parts, hipStre
   a.cu = s.cu;
   a.n_seqs = s.n_seqs;
   a.korder = s.cu ? reinterpret_cast<const int32_t *>(p.ws + L.korder) : nullptr;
+  a.qorder = s.cu ? reinterpret_cast<const int32_t *>(p.ws + L.qorder) : nullptr;
   a.ksplit = 1;
   a.dkv_part = reinterpret_cast<float *>(p.ws + L.part);
   a.qsplit = 1;
@@ -994,6 +930,18 @@ int launch_attn_bwd(const AttnShape &s, const AttnBwdPtrs &p, int parts, hipStre
       if ((rc = launch_to_trans(p.k, s.k_stride, s.hkv, s.d, s.N, ws_kt, stream))) return rc;
       if ((rc = launch_to_trans(p.q, s.q_stride, s.hq, s.d, s.N, ws_qt, stream))) return rc;
       if ((rc = launch_to_trans(p.dout, p.do_stride, s.hq, s.d, s.N, ws_dot, stream))) return rc;
+    }
+    // Over packed documents, the block orders of both kernels (the dK/dV
+    // kernel, run alone, reads its order from the workspace as left here).
+    if (s.cu) {
+      const int q_bs = s.d == 128 ? (hpw == 4 ? DqCfg<128, 4, 2>::BM : hpw == 2 ? DqCfg<128, 2, 4>::BM
+                                                                              : DqCfg<128, 1, 8>::BM)
+                                  : (hpw == 4 ? DqCfg<64, 4, 2>::BM : hpw == 2 ? DqCfg<64, 2, 4>::BM
+                                                                             : DqCfg<64, 1, 8>::BM);
+      const int k_bs = s.d == 128 ? DkvCfg<128>::BNK : DkvCfg<64>::BNK;
+      if ((rc = launch_block_orders(s.cu, s.n_seqs, s.N, s.causal, q_bs, reinterpret_cast<int32_t *>(p.ws + L.qorder),
+                                    k_bs, reinterpret_cast<int32_t *>(p.ws + L.korder), stream)))
+        return rc;
     }
     if (s.d == 128)
       rc = hpw == 4 ? launch_dq_cfg<128, 4, 2>(a, stream)

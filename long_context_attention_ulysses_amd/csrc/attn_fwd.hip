@@ -22,9 +22,10 @@
 //     log2 domain, p = exp2(s*scale*log2e - m), O^T += V^T P^T with P^T taken
 //     straight from the score registers.
 //   * Workgroups are issued heaviest-first (last query blocks first under the
-//     causal mask), and consecutive workgroup ids alternate GQA groups, so the
-//     round-robin assignment of ids to the 8 XCDs keeps one KV head per XCD L2
-//     whenever the number of groups divides 8.
+//     causal mask; over packed documents in the order a small sorting pass
+//     writes into the workspace), and consecutive workgroup ids alternate GQA
+//     groups, so the round-robin assignment of ids to the 8 XCDs keeps one KV
+//     head per XCD L2 whenever the number of groups divides 8.
 //   * With fewer than 512 (query block, head group) pairs, each pair's key
 //     tiles are split over up to 4 workgroups that write their float32
 //     softmax states (unnormalised O, running max, sum); a merge pass combines
@@ -49,6 +50,7 @@ struct FwdArgs {
   int causal;
   const int32_t *cu;
   int n_seqs;
+  int32_t *qorder;               // packed documents: query blocks by decreasing work
   int qsplit;                    // workgroups per (query block, head group)
   float *opart, *mpart, *lpart;  // partials when qsplit > 1: O [s][N][hq][D], max and sum [s][hq][N]
 };
@@ -84,11 +86,13 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_fwd_kernel(FwdArgs a) {
   const int l32 = lane & 31;
   const int hi32 = lane >> 5;
 
-  // Heaviest query blocks first; consecutive ids alternate head groups, and
-  // with a split the pieces of one query block are consecutive.
+  // Heaviest query blocks first (the last ones under a causal mask, the
+  // sorted order over packed documents); consecutive ids alternate head
+  // groups, and with a split the pieces of one query block are consecutive.
   const int item = blockIdx.x;
   const int hg = item % a.nhg;
-  const int qb = a.nqb - 1 - (kSplit ? item / a.nhg / a.qsplit : item / a.nhg);
+  const int qbi = kSplit ? item / a.nhg / a.qsplit : item / a.nhg;
+  const int qb = a.qorder ? a.qorder[qbi] : a.nqb - 1 - qbi;
   const int split = kSplit ? item / a.nhg % a.qsplit : 0;
   const int64_t q0 = (int64_t)qb * C::BM;
   const int h = hg * HPW + w / RB;
@@ -360,6 +364,10 @@ int launch_fwd_cfg(FwdArgs a, hipStream_t stream) {
   a.nqb = (int)((a.N + C::BM - 1) / C::BM);
   a.nhg = a.hq / HPW;
   a.qsplit = fwd_ksplit(a.N, a.hq, a.hq / a.G);
+  if (a.qorder) {
+    const int rc = launch_block_orders(a.cu, a.n_seqs, a.N, a.causal, C::BM, a.qorder, 0, nullptr, stream);
+    if (rc) return rc;
+  }
   const int64_t blocks = (int64_t)a.nqb * a.nhg * a.qsplit;
   if (a.qsplit > 1)
     hipLaunchKernelGGL((attn_fwd_kernel<D, HPW, RB, true>), dim3((unsigned)blocks), dim3(C::NT), 0, stream, a);
@@ -411,6 +419,8 @@ int launch_attn_fwd(const AttnShape &s, const bf16_t *q, const bf16_t *k, const 
   a.causal = s.causal;
   a.cu = s.cu;
   a.n_seqs = s.n_seqs;
+  a.qorder = s.cu ? reinterpret_cast<int32_t *>(static_cast<char *>(ws) + fwd_ws_order(s.N, s.hq, s.hkv, s.d))
+                  : nullptr;
   a.nqb = a.nhg = 0;
   {
     const int ks = fwd_ksplit(s.N, s.hq, s.hkv);

@@ -23,6 +23,13 @@ __host__ __device__ inline int64_t pad64(int64_t n) { return (n + 63) / 64 * 64;
 
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
+// Over packed documents: q_order (if not null) receives the ids of the
+// blocks of q_bs queries by decreasing number of 64-key tiles in their key
+// ranges, k_order (if not null) those of the blocks of k_bs keys by
+// decreasing number of 64-query tiles in their query ranges.
+int launch_block_orders(const int32_t *cu, int n_seqs, int64_t N, int causal, int q_bs, int32_t *q_order,
+                        int k_bs, int32_t *k_order, hipStream_t stream);
+
 // Writes xt[h][d][pad64(N)]: the contraction-ordered, transposed copy of the
 // `heads` heads of x (token stride xs), zero beyond N.
 int launch_to_trans(const bf16_t *x, int64_t xs, int heads, int d, int64_t N, bf16_t *xt,
@@ -47,13 +54,17 @@ inline int fwd_ksplit(int64_t N, int hq, int hkv) {
 
 // Forward workspace: V^T [hkv][d][pad64(N)] bf16, then, when the forward
 // splits its key ranges, float32 partials: O [s][N][hq][d], max [s][hq][N],
-// sum [s][hq][N].
+// sum [s][hq][N], then the int32 order of the query blocks for packed
+// documents (pad64(N) / 64 entries).
 inline size_t fwd_ws_part(int64_t N, int hkv, int d) {
   return align256((size_t)hkv * d * pad64(N) * sizeof(bf16_t));
 }
-inline size_t fwd_ws_bytes(int64_t N, int hq, int hkv, int d) {
+inline size_t fwd_ws_order(int64_t N, int hq, int hkv, int d) {
   const int s = fwd_ksplit(N, hq, hkv);
   return fwd_ws_part(N, hkv, d) + (s > 1 ? align256((size_t)s * N * hq * (d + 2) * 4) : 0);
+}
+inline size_t fwd_ws_bytes(int64_t N, int hq, int hkv, int d) {
+  return fwd_ws_order(N, hq, hkv, d) + align256((size_t)pad64(N) / 64 * 4);
 }
 
 // Number of workgroups the dK/dV kernel splits each (128-key block, KV head)
@@ -74,12 +85,13 @@ inline int dq_ksplit(int64_t N, int hq, int hkv) { return fwd_ksplit(N, hq, hkv)
 
 // Backward workspace regions (byte offsets): D and LSE*log2(e) as float
 // [hq][pad64(N)], then K^T, Q^T, dO^T as contraction-ordered bf16 copies,
-// then the int32 order of the dK/dV kernel's key blocks for packed
-// documents (pad64(N) / 64 entries), then, when the dK/dV kernel splits its
+// then the int32 orders of the dK/dV kernel's key blocks and of the dq
+// kernel's query blocks for packed documents (pad64(N) / 64 entries each),
+// then, when the dK/dV kernel splits its
 // query ranges, the float32 partials [ksplit][N][hkv][dK, dV][d], and when
 // the dq kernel splits its key ranges, the float32 partials [s][N][hq][d].
 struct BwdWs {
-  size_t delta, lse2, kt, qt, dot, korder, part, qpart, total;
+  size_t delta, lse2, kt, qt, dot, korder, qorder, part, qpart, total;
 };
 
 inline BwdWs bwd_ws_layout(int64_t N, int hq, int hkv, int d) {
@@ -91,7 +103,8 @@ inline BwdWs bwd_ws_layout(int64_t N, int hq, int hkv, int d) {
   w.qt = w.kt + align256((size_t)hkv * d * np * 2);
   w.dot = w.qt + align256((size_t)hq * d * np * 2);
   w.korder = w.dot + align256((size_t)hq * d * np * 2);
-  w.part = w.korder + align256(np / 64 * 4);
+  w.qorder = w.korder + align256(np / 64 * 4);
+  w.part = w.qorder + align256(np / 64 * 4);
   const int ks = dkdv_ksplit(N, hkv);
   w.qpart = w.part + (ks > 1 ? align256((size_t)ks * N * hkv * 2 * d * 4) : 0);
   const int qs = dq_ksplit(N, hq, hkv);

@@ -126,8 +126,9 @@ def test_attn_fwd_noalloc_validation():
     assert L.attn_fwd_workspace_bytes(1 << 18, 4, 1, 128) <= limit
     assert L.attn_fwd_workspace_bytes(1 << 18, 8, 2, 128) > limit
     assert fwd(N=1 << 18, hq=8, hkv=2, qs=12 * 128) == uly.CODE["ULY_E_SCRATCH"]
-    assert L.attn_fwd_workspace_bytes(327680, 4, 1, 128) <= limit < L.attn_fwd_workspace_bytes(327744, 4, 1, 128)
-    assert fwd(N=327744, hq=4, hkv=1, qs=6 * 128) == uly.CODE["ULY_E_SCRATCH"]
+    assert L.attn_fwd_workspace_bytes(327552, 4, 1, 128) <= limit < L.attn_fwd_workspace_bytes(327616, 4, 1, 128)
+    assert L.attn_fwd_workspace_bytes(163776, 8, 2, 128) <= limit < L.attn_fwd_workspace_bytes(163840, 8, 2, 128)
+    assert fwd(N=327616, hq=4, hkv=1, qs=6 * 128) == uly.CODE["ULY_E_SCRATCH"]
     assert "scratch" in uly.status_string(uly.CODE["ULY_E_SCRATCH"])
 
 
@@ -142,8 +143,10 @@ def test_attn_varlen_and_bwd_validation():
     need = L.attn_bwd_workspace_bytes(N, hq, hkv, d, 1)
     assert need >= N * hq * 4 * 2 + N * d * (hkv + 2 * hq) * 2 and need % 256 == 0
     # transposed V, plus float32 partial softmax states (O, max, sum) of the
-    # 4-way key split that 1024 tokens (32 query blocks x 2 head groups) get
-    assert L.attn_fwd_workspace_bytes(N, hq, hkv, d) == hkv * d * N * 2 + 4 * N * hq * (d + 2) * 4
+    # 4-way key split that 1024 tokens (32 query blocks x 2 head groups) get,
+    # plus the 16 int32 entries of the packed-document query-block order
+    # (rounded up to 256 bytes)
+    assert L.attn_fwd_workspace_bytes(N, hq, hkv, d) == hkv * d * N * 2 + 4 * N * hq * (d + 2) * 4 + 256
 
     def bwd(ws=W, ws_bytes=need, dq=9 << 25, dk=10 << 25, dv=11 << 25):
         return L.attn_bwd(A, B, C, D_, E, F, dq, dk, dv, N, hq, hkv, d, 1536, 1536, 1536, 1024, 1024,
@@ -173,10 +176,10 @@ def test_workspaces_grow_linearly_with_n():
             dkdv_split = N // 128 * hkv < 512
             dq_split = N // 64 * (hq // 4) < 512  # 4 heads per dq workgroup here
             split_max = (4 * N * hkv * 2 * d * 4 if dkdv_split else 0) + (4 * N * hq * d * 4 if dq_split else 0)
-            assert f1 <= hkv * d * N * 2 + (4 * N * hq * (d + 2) * 4 if dq_split else 0) + 512
+            assert f1 <= hkv * d * N * 2 + (4 * N * hq * (d + 2) * 4 if dq_split else 0) + N // 64 * 4 + 512
             if not dq_split:
                 assert f2 == 2 * f1
-            assert b1 <= N * (2 * hq * 4 + (hkv + 2 * hq) * d * 2) + N // 64 * 4 + split_max + 2048
+            assert b1 <= N * (2 * hq * 4 + (hkv + 2 * hq) * d * 2) + 2 * (N // 64 * 4) + split_max + 2048
             if not dkdv_split and not dq_split:
                 assert abs(b2 - 2 * b1) <= 2048
 
