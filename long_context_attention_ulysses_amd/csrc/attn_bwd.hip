@@ -127,12 +127,13 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_bwd_dq_kernel(BwdArgs a
   const int64_t r0 = q0 + (int64_t)(w % RB) * 32;
 
   const int64_t q_last = (q0 + C::BM < a.N ? q0 + C::BM : a.N) - 1;
-  const int64_t kv_lo = key_range(a.cu, a.n_seqs, a.N, a.causal, q0).lo;
-  const int64_t kv_hi = key_range(a.cu, a.n_seqs, a.N, a.causal, q_last).hi;
+  const int b0 = doc_start(a.cu, a.n_seqs, q0);  // documents found from the block's first row on
+  const int64_t kv_lo = key_range_from(a.cu, a.n_seqs, a.N, a.causal, b0, q0).lo;
+  const int64_t kv_hi = key_range_from(a.cu, a.n_seqs, a.N, a.causal, b0, q_last).hi;
   const bool wave_valid = r0 < a.N;
   const int64_t w_last = (r0 + 32 < a.N ? r0 + 32 : a.N) - 1;
-  const KeyRange wr0 = key_range(a.cu, a.n_seqs, a.N, a.causal, wave_valid ? r0 : 0);
-  const KeyRange wr1 = key_range(a.cu, a.n_seqs, a.N, a.causal, wave_valid ? w_last : 0);
+  const KeyRange wr0 = key_range_from(a.cu, a.n_seqs, a.N, a.causal, b0, wave_valid ? r0 : q0);
+  const KeyRange wr1 = key_range_from(a.cu, a.n_seqs, a.N, a.causal, b0, wave_valid ? w_last : q0);
   const int64_t w_lo = wr0.lo, w_hi = wr1.hi;
   const int64_t w_lo_max = wr1.lo, w_hi_min = wr0.hi;
 
@@ -140,7 +141,7 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_bwd_dq_kernel(BwdArgs a
   const bool row_ok = row < a.N;
   int64_t rlo = 0, rhi = 0;
   if (row_ok) {
-    const KeyRange kr = key_range(a.cu, a.n_seqs, a.N, a.causal, row);
+    const KeyRange kr = key_range_from(a.cu, a.n_seqs, a.N, a.causal, b0, row);
     rlo = kr.lo;
     rhi = kr.hi;
   }
@@ -428,10 +429,11 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
   const bool wave_valid = kw0 < a.N;
   const int64_t kw_last = (kw0 + 32 < a.N ? kw0 + 32 : a.N) - 1;
 
-  const int64_t qr_lo = query_range(a.cu, a.n_seqs, a.N, a.causal, k0).lo;
-  const int64_t qr_hi = query_range(a.cu, a.n_seqs, a.N, a.causal, k_last).hi;
-  const KeyRange wq0 = query_range(a.cu, a.n_seqs, a.N, a.causal, wave_valid ? kw0 : 0);
-  const KeyRange wq1 = query_range(a.cu, a.n_seqs, a.N, a.causal, wave_valid ? kw_last : 0);
+  const int b0 = doc_start(a.cu, a.n_seqs, k0);  // documents found from the block's first key on
+  const int64_t qr_lo = query_range_from(a.cu, a.n_seqs, a.N, a.causal, b0, k0).lo;
+  const int64_t qr_hi = query_range_from(a.cu, a.n_seqs, a.N, a.causal, b0, k_last).hi;
+  const KeyRange wq0 = query_range_from(a.cu, a.n_seqs, a.N, a.causal, b0, wave_valid ? kw0 : k0);
+  const KeyRange wq1 = query_range_from(a.cu, a.n_seqs, a.N, a.causal, b0, wave_valid ? kw_last : k0);
   const int64_t w_lo = wq0.lo, w_hi = wq1.hi;
   const int64_t w_lo_max = wq1.lo, w_hi_min = wq0.hi;
 
@@ -439,7 +441,7 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
   const bool key_ok = key < a.N;
   int64_t qlo = 0, qhi = 0;
   if (key_ok) {
-    const KeyRange qr = query_range(a.cu, a.n_seqs, a.N, a.causal, key);
+    const KeyRange qr = query_range_from(a.cu, a.n_seqs, a.N, a.causal, b0, key);
     qlo = qr.lo;
     qhi = qr.hi;
   }

@@ -335,4 +335,49 @@ __host__ __device__ __forceinline__ KeyRange query_range(const int32_t *cu, int 
   return clamp_range(r, N);
 }
 
+// The same ranges for a token i when the document b of a token at or
+// before i is known (b = doc_start(t0) with t0 <= i): the document of i is
+// found by scanning forward from b, since the rows of one block cross few
+// document boundaries, instead of by a binary search per token. For a valid
+// table the ranges equal key_range / query_range; for any table b stays in
+// [b, n_seqs - 1], so the table reads and the clamped range stay in bounds.
+__host__ __device__ __forceinline__ int doc_start(const int32_t *cu, int n_seqs, int64_t t0) {
+  return cu ? doc_of(cu, n_seqs, t0) : 0;
+}
+
+__host__ __device__ __forceinline__ int doc_after(const int32_t *cu, int n_seqs, int b, int64_t t) {
+  while (b + 1 < n_seqs && (int64_t)cu[b + 1] <= t) ++b;
+  return b;
+}
+
+__host__ __device__ __forceinline__ KeyRange key_range_from(const int32_t *cu, int n_seqs, int64_t N, int causal,
+                                                            int b, int64_t i) {
+  KeyRange r;
+  if (cu) {
+    b = doc_after(cu, n_seqs, b, i);
+    r.lo = cu[b];
+    r.hi = cu[b + 1];
+  } else {
+    r.lo = 0;
+    r.hi = N;
+  }
+  if (causal) r.hi = i + 1;
+  return clamp_range(r, N);
+}
+
+__host__ __device__ __forceinline__ KeyRange query_range_from(const int32_t *cu, int n_seqs, int64_t N, int causal,
+                                                              int b, int64_t j) {
+  KeyRange r;
+  if (cu) {
+    b = doc_after(cu, n_seqs, b, j);
+    r.lo = cu[b];
+    r.hi = cu[b + 1];
+  } else {
+    r.lo = 0;
+    r.hi = N;
+  }
+  if (causal) r.lo = j;
+  return clamp_range(r, N);
+}
+
 }  // namespace uly

@@ -99,14 +99,16 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_fwd_kernel(FwdArgs a) {
   const int g = (hg * HPW) / a.G;
   const int64_t r0 = q0 + (int64_t)(w % RB) * 32;
 
-  // Key range of the workgroup and of this wave.
+  // Key range of the workgroup and of this wave (documents found from the
+  // block's first row on).
   const int64_t q_last = (q0 + C::BM < a.N ? q0 + C::BM : a.N) - 1;
-  const int64_t kv_lo = key_range(a.cu, a.n_seqs, a.N, a.causal, q0).lo;
-  const int64_t kv_hi = key_range(a.cu, a.n_seqs, a.N, a.causal, q_last).hi;
+  const int b0 = doc_start(a.cu, a.n_seqs, q0);
+  const int64_t kv_lo = key_range_from(a.cu, a.n_seqs, a.N, a.causal, b0, q0).lo;
+  const int64_t kv_hi = key_range_from(a.cu, a.n_seqs, a.N, a.causal, b0, q_last).hi;
   const bool wave_valid = r0 < a.N;
   const int64_t w_last = (r0 + 32 < a.N ? r0 + 32 : a.N) - 1;
-  const KeyRange wr0 = key_range(a.cu, a.n_seqs, a.N, a.causal, wave_valid ? r0 : 0);
-  const KeyRange wr1 = key_range(a.cu, a.n_seqs, a.N, a.causal, wave_valid ? w_last : 0);
+  const KeyRange wr0 = key_range_from(a.cu, a.n_seqs, a.N, a.causal, b0, wave_valid ? r0 : q0);
+  const KeyRange wr1 = key_range_from(a.cu, a.n_seqs, a.N, a.causal, b0, wave_valid ? w_last : q0);
   const int64_t w_lo = wr0.lo, w_hi = wr1.hi;          // union of the rows' ranges
   const int64_t w_lo_max = wr1.lo, w_hi_min = wr0.hi;  // intersection
 
@@ -115,7 +117,7 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_fwd_kernel(FwdArgs a) {
   const bool row_ok = row < a.N;
   int64_t rlo = 0, rhi = 0;
   if (row_ok) {
-    const KeyRange kr = key_range(a.cu, a.n_seqs, a.N, a.causal, row);
+    const KeyRange kr = key_range_from(a.cu, a.n_seqs, a.N, a.causal, b0, row);
     rlo = kr.lo;
     rhi = kr.hi;
   }

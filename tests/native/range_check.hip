@@ -19,6 +19,21 @@ static int check(const int32_t *cu, int n_seqs, int64_t N, bool valid) {
                  (long long)r.hi);
           ++bad;
         }
+      // the scanning variants from the document of every earlier token
+      for (int64_t t0 = 0; t0 <= t; ++t0) {
+        const int b0 = uly::doc_start(cu, n_seqs, t0);
+        const KeyRange kf = uly::key_range_from(cu, n_seqs, N, causal, b0, t);
+        const KeyRange qf = uly::query_range_from(cu, n_seqs, N, causal, b0, t);
+        for (const KeyRange &r : {kf, qf})
+          if (r.lo < 0 || r.hi > N || r.lo > r.hi) {
+            printf("out of range (scan from %lld): t=%lld causal=%d\n", (long long)t0, (long long)t, causal);
+            ++bad;
+          }
+        if (valid && (kf.lo != k.lo || kf.hi != k.hi || qf.lo != q.lo || qf.hi != q.hi)) {
+          printf("scan differs: t0=%lld t=%lld causal=%d\n", (long long)t0, (long long)t, causal);
+          ++bad;
+        }
+      }
       if (valid) {
         int b = 0;
         while (cu[b + 1] <= t) ++b;
@@ -34,11 +49,13 @@ static int check(const int32_t *cu, int n_seqs, int64_t N, bool valid) {
 
 int main() {
   const int32_t good[] = {0, 3, 4, 10, 16};
+  const int32_t singles[] = {0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16};  // one token each
   const int32_t past_end[] = {0, 5, 40};          // last document ends past N = 16
   const int32_t negative[] = {-7, 2, 16};
   const int32_t unsorted[] = {0, 12, 5, 16};
   const int32_t huge[] = {0, 2147483647};
   int bad = check(good, 4, 16, true);
+  bad += check(singles, 16, 16, true);
   bad += check(past_end, 2, 16, false);
   bad += check(negative, 2, 16, false);
   bad += check(unsorted, 3, 16, false);

@@ -1,7 +1,10 @@
 """The attention kernels' key/query range helpers, built for the host with
 hipcc: ranges stay inside [0, N) for any cu_seqlens table, so a table the
 host did not check gives wrong values rather than out-of-range tile
-addresses, and valid tables give each token's document range."""
+addresses, and valid tables give each token's document range. The scanning
+variants the kernels use (document found from that of an earlier token)
+give the same ranges as the binary search for valid tables, from every
+earlier token, and stay in bounds for invalid ones."""
 import os
 import shutil
 import subprocess
