@@ -78,16 +78,26 @@ def test_accumulate_adds_weight_gradients():
 
 def test_full_size_sampled_rows():
     """Qwen3-4B MLP shape (H = 2560, I = 9728) on 2048 tokens in tiles of
-    512; rows are independent, so sampled rows of y and dx are checked
-    against the oracle one by one."""
+    512. Token rows are independent, so sampled rows of y and dx are checked
+    against the oracle one by one. The weight gradients of intermediate unit
+    j (rows j and I + j of dW_gu, column j of dW_down) depend only on x, dy
+    and that unit's own weights, so the oracle run over all 2048 tokens with
+    only the sampled units' weights gives their exact values."""
     n, H, I = 2048, 2560, 9728
     m = Mlp(n, H, I, seed=21)
-    y, dx, _, _ = m.run(512)
+    y, dx, dwg, dwd = m.run(512)
     rows = np.array([0, 1, 511, 512, 1000, 2047])
     y_ref = oracle.swiglu_mlp(m.x_b[rows], m.wg_b, m.wd_b)
     dx_ref, _, _ = oracle.swiglu_mlp_bwd(m.x_b[rows], m.wg_b, m.wd_b, m.dy_b[rows])
     assert_close("y rows", oracle.bf16_to_f64(y[rows]), y_ref, FWD_MAX_ABS, FWD_REL)
     assert_close("dx rows", oracle.bf16_to_f64(dx[rows]), dx_ref, GRAD_MAX_ABS, GRAD_REL)
+    units = np.array([0, 1, 2047, 4864, 9000, I - 1])
+    gu_rows = np.concatenate([units, I + units])
+    _, dwg_ref, dwd_ref = oracle.swiglu_mlp_bwd(m.x_b, m.wg_b[gu_rows], m.wd_b[:, units], m.dy_b)
+    dwg_s = dwg.cpu().numpy().astype(np.float64)[gu_rows]
+    dwd_s = dwd.cpu().numpy().astype(np.float64)[:, units]
+    assert_close("dW_gu units", dwg_s, dwg_ref, GRAD_MAX_ABS * np.abs(dwg_ref).max(), GRAD_REL)
+    assert_close("dW_down units", dwd_s, dwd_ref, GRAD_MAX_ABS * np.abs(dwd_ref).max(), GRAD_REL)
 
 
 def test_mlp_argument_errors():
