@@ -540,7 +540,8 @@ def short_kernel_name(full: str) -> str:
 
 def write_traffic_summary(workload: str, pmc_dir: str):
     """Turn the rocprofv3 counter runs of `bench.py --steps 2 --warmup 1`
-    into profiles/traffic_<workload>.txt:
+    into profiles/traffic_<workload>.txt (the dispatches of the bench steps:
+    warm-up, timed steps and breakdown pass):
       - FETCH_SIZE in <pmc_dir>/fetch_counter_collection.csv and WRITE_SIZE in
         <pmc_dir>/write_counter_collection.csv: HBM bytes per dispatch. Both
         counters are scaled by what they read for the step's first launch,
@@ -603,11 +604,21 @@ def write_traffic_summary(workload: str, pmc_dir: str):
         "source_sha256": csrc_digest(),
         "dispatches": [],
     }
+    # Only the bench steps' dispatches: the first kernel that is not the
+    # library's (torch's fill before the swaps timed alone) ends them.
+    lib_kernels = ("swap_kernel", "to_trans_kernel", "attn_", "fwd_merge_kernel", "dq_part_sum_kernel",
+                   "dkdv_part_sum_kernel", "block_order_kernel")
     for (d, k, fv), (_, _, wv) in zip(fetch, write):
+        if not k.startswith(lib_kernels):
+            doc["dispatches_left_out"] = len(fetch) - len(doc["dispatches"])
+            break
         e = {"dispatch": d, "kernel": k, "fetch_kb": fv, "write_kb": wv,
              "hbm_bytes": int(round((fv * fetch_scale + wv * write_scale) * 1024))}
         if d in clocks:
-            e["clock_ghz"] = round(clocks[d][0], 4)
+            # the counter's window is only meaningful against dispatches of a
+            # millisecond or more (short ones read above the 2.4 GHz maximum)
+            if clocks[d][1] >= 1_000_000:
+                e["clock_ghz"] = round(clocks[d][0], 4)
             e["duration_ns"] = clocks[d][1]
         doc["dispatches"].append(e)
     out = os.path.join(ROOT, "profiles", "traffic_%s.txt" % workload)
