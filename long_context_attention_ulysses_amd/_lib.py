@@ -344,7 +344,9 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, scale: float, causal: bool = Tru
 
 def attn_bwd_dq(q, k, v, o, lse, dout, dq, scale: float, causal: bool = True, ws=None, cu_seqlens=None,
                 stream=None) -> None:
-    """First step of attn_bwd: D = rowsum(dout * o) into ws, and dq."""
+    """First step of attn_bwd: D = rowsum(dout * o) and LSE*log2(e) into ws
+    (with, at d = 64, the transposed copies and, over packed documents, both
+    steps' block orders), and dq."""
     a = _Args("attn_bwd_dq")
     N, hq, hkv, d = _qkv_dims(q, k)
     st, st_o, st_do = _bwd_args(a, q, k, v, o, lse, dout, N, hq, hkv, d)
@@ -358,9 +360,10 @@ def attn_bwd_dq(q, k, v, o, lse, dout, dq, scale: float, causal: bool = True, ws
 
 def attn_bwd_dkdv(q, k, v, lse, dout, dk, dv, scale: float, causal: bool = True, ws=None, cu_seqlens=None,
                   stream=None) -> None:
-    """Second step of attn_bwd: dk and dv, reading D, LSE and the transposed
-    copies from ws (left there by attn_bwd_dq) and overwriting ws's key-block
-    order and dK/dV partial regions (so concurrent calls need their own ws)."""
+    """Second step of attn_bwd: dk and dv, reading D, LSE, the transposed
+    copies and the key-block order from ws (left there by attn_bwd_dq) and
+    overwriting ws's dK/dV partial region (so concurrent calls need their own
+    ws)."""
     a = _Args("attn_bwd_dkdv")
     N, hq, hkv, d = _qkv_dims(q, k)
     st, _, st_do = _bwd_args(a, q, k, v, None, lse, dout, N, hq, hkv, d)
