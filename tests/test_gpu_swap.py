@@ -37,12 +37,11 @@ def _unpack(r_bits, P, segs):
     (5, 3, [3, 6], 8),
     (11, 8, [8], 24),
     (50, 1, [4, 2, 2], 16),
-    # token rows of 6144 and 4096 16-byte vectors: just past and at the
-    # token-major kernel's index-table limit
+    # long token rows (6144 and 4096 16-byte vectors, 96 and 64 KiB)
     (37, 4, [256, 64, 64], 128),
     (9, 8, [128, 64, 64], 128),
-    # rows past the table limit with more (chunk, segment) runs than one
-    # launch of the run-major kernel takes (48 and 96 runs: 2 and 3 launches)
+    # many chunks: P = 16 and 32, segment blocks of 16/4/4 and 8/2/2 heads
+    # (48 and 96 runs per token row)
     (3, 16, [256, 64, 64], 128),
     (2, 32, [256, 64, 64], 128),
 ])
