@@ -261,16 +261,20 @@ def test_unsplit_grids_sampled(N, hq, hkv, d):
         assert np.all(np.isfinite(oracle.bf16_to_f64(t))), nm + " has unwritten/non-finite elements"
 
 
-def test_long_packed_batch_sampled():
-    """2.1 M tokens in short documents: more key blocks than the dK/dV
-    kernel's work sort takes (it keeps key order then), grids of over 16000
-    workgroups and the largest row offsets the tests reach; oracle on sampled
-    rows and on the first and last 128 keys."""
-    N, hq, hkv, d = 2_100_000, 2, 1, 64
-    rng = np.random.default_rng(0x10C)
+@pytest.mark.parametrize("N,max_len", [(2_100_000, 1200), (400_000, 1200), (1_000_000, 200)])
+def test_long_packed_batch_sampled(N, max_len):
+    """Long batches of short documents: at 2.1 M tokens more blocks than the
+    work sort of the workgroup-order pass takes (the kernels keep block
+    order), grids of over 16000 workgroups and the largest row offsets the
+    tests reach; at 400 K tokens (about 3100 blocks per order) and 1 M tokens
+    in documents of at most 200 tokens (about 7800 blocks, 9990 documents)
+    sorted orders of several thousand blocks. Oracle on sampled rows and on
+    the first and last 128 keys."""
+    hq, hkv, d = 2, 1, 64
+    rng = np.random.default_rng(0x10C + N)
     lens = []
     while sum(lens) < N:
-        lens.append(int(rng.integers(1, 1201)))
+        lens.append(int(rng.integers(1, max_len + 1)))
     lens[-1] -= sum(lens) - N
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     print("long packed batch N=%d docs=%d" % (N, len(lens)), flush=True)
