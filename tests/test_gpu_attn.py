@@ -96,6 +96,8 @@ SMALL = [
     (65, 8, 1, 128, True, None, 0.5),                               # one row past a tile, G = 8
     (129, 6, 2, 64, True, None, 1.0),                               # G = 3, d = 64
     (200, 4, 1, 128, True, [0, 1, 2, 3, 67, 130, 131, 200], 0.5),  # one-token documents
+    (300, 4, 1, 128, False, None, 0.5),                             # non-causal, d = 128, G = 4
+    (384, 8, 2, 128, False, [0, 100, 101, 384], 0.5),               # non-causal documents, d = 128
 ]
 
 
