@@ -531,6 +531,22 @@ def measured_profile(workload: str, step_name: str):
     return out
 
 
+def add_measured_profile(workload: str, roofline: dict):
+    """traffic (HBM bytes per launch) and the clock of the roofline kernel from
+    the committed counter summary of this workload, with the fraction of the
+    peak at that clock; traffic None when there is no summary of the current
+    sources."""
+    prof = measured_profile(workload, roofline["kernel"])
+    roofline["traffic"] = prof and prof["hbm_bytes"]
+    if prof and prof.get("clock_ghz"):
+        # clock measured by the committed counter pass of the same sources
+        ghz = prof["clock_ghz"]
+        roofline["clock_ghz"] = ghz
+        roofline["peak_at_clock"] = round(BF16_PEAK_TFLOPS * ghz / PEAK_CLOCK_GHZ, 1)
+        roofline["frac_clock_adjusted"] = round(roofline["achieved"] / roofline["peak_at_clock"], 4)
+        roofline["clock_source"] = prof["clock_source"]
+
+
 def short_kernel_name(full: str) -> str:
     """'void uly::(anonymous namespace)::f<128, 4>(args)' -> 'f<128, 4>'."""
     name = full.replace("(anonymous namespace)::", "")
@@ -579,8 +595,13 @@ def write_traffic_summary(workload: str, pmc_dir: str):
         for d, _, cyc in grbm:
             if dur.get(d, 0) > 0:
                 clocks[d] = (cyc / 8.0 / dur[d], dur[d])   # cycles per ns = GHz
+    # The bench steps start at the first seq->head pack (runtime copies, e.g.
+    # of a cu_seqlens table, can come before it).
+    lib_kernels = ("swap_kernel", "to_trans_kernel", "attn_", "fwd_merge_kernel", "dq_part_sum_kernel",
+                   "dkdv_part_sum_kernel", "block_order_kernel")
+    first = next(i for i, (_, k, _) in enumerate(fetch) if k.startswith("swap_kernel"))
+    fetch, write = fetch[first:], write[first:]
     shard_bytes = w.n * w.Ht * w.d * 2
-    assert fetch[0][1].startswith("swap"), fetch[0][1]
     fetch_scale = shard_bytes / (fetch[0][2] * 1024)
     write_scale = shard_bytes / (write[0][2] * 1024)
     run = ("-- python3 $REPO/bench.py --workload %s --steps 2 --warmup 1 --cpu-tokens 0 --no-ring --no-loss "
@@ -606,8 +627,6 @@ def write_traffic_summary(workload: str, pmc_dir: str):
     }
     # Only the bench steps' dispatches: the first kernel that is not the
     # library's (torch's fill before the swaps timed alone) ends them.
-    lib_kernels = ("swap_kernel", "to_trans_kernel", "attn_", "fwd_merge_kernel", "dq_part_sum_kernel",
-                   "dkdv_part_sum_kernel", "block_order_kernel")
     for (d, k, fv), (_, _, wv) in zip(fetch, write):
         if not k.startswith(lib_kernels):
             doc["dispatches_left_out"] = len(fetch) - len(doc["dispatches"])
@@ -677,15 +696,7 @@ def main():
         "data": "synthetic",
         "config": r.pop("config"),
     }
-    prof = measured_profile(args.workload, r["roofline"]["kernel"])
-    r["roofline"]["traffic"] = prof and prof["hbm_bytes"]
-    if prof and prof.get("clock_ghz"):
-        # clock measured by the committed counter pass of the same sources
-        ghz = prof["clock_ghz"]
-        r["roofline"]["clock_ghz"] = ghz
-        r["roofline"]["peak_at_clock"] = round(BF16_PEAK_TFLOPS * ghz / PEAK_CLOCK_GHZ, 1)
-        r["roofline"]["frac_clock_adjusted"] = round(r["roofline"]["achieved"] / r["roofline"]["peak_at_clock"], 4)
-        r["roofline"]["clock_source"] = prof["clock_source"]
+    add_measured_profile(args.workload, r["roofline"])
     result["roofline"] = r.pop("roofline")
     for key in ("value", "ms_per_step"):
         r.pop(key)
@@ -696,6 +707,7 @@ def main():
             steps = 3 if name == "256k" else 10
             log("workload %s (%d steps) ..." % (name, steps))
             wr = measure_workload(uly, torch, workloads.WORKLOADS[name], steps, 2, swaps_alone=False)
+            add_measured_profile(name, wr["roofline"])
             result["workloads"][name] = {
                 "config": wr["config"]["workload"], "steps": steps, "ms_per_step": wr["ms_per_step"],
                 "value_tflops": wr["value"], "attn_tflops": wr["attn_tflops"], "attn_frac_peak": wr["attn_frac_peak"],
