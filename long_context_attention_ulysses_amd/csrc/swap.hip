@@ -16,11 +16,14 @@
 // chunk row. The token, the chunk and k come from two multiply-shift
 // divisions and the source vector from a walk over the (at most 8) segments,
 // so no index table is built and nothing but registers limits how many
-// blocks a CU holds. Loads and stores are nontemporal: every byte is touched
-// once. One vector per thread with 256-thread blocks measured faster than 2
-// or 4 vectors in flight per thread, than per-block LDS index tables, than a
-// walk in chunk-tensor order and than skewing the chunks' tokens against
-// each other. Indexes are 32-bit: the boundary rejects tensors of 2^31
+// blocks a CU holds. Every byte is touched once, so loads are nontemporal and
+// stores are nontemporal at agent scope (sc1): they write through the XCD's L2
+// instead of leaving dirty lines there to be evicted later, which measured 4
+// to 14 % faster than nontemporal stores alone on a cold L2; the load's scope
+// bits made no difference. One vector per thread with 256-thread blocks
+// measured faster than 2 or 4 vectors in flight per thread, than per-block
+// LDS index tables, than a walk in chunk-tensor order and than skewing the
+// chunks' tokens against each other. Indexes are 32-bit: the boundary rejects tensors of 2^31
 // vectors or more.
 #include "uly_common.h"
 #include "uly_internal.h"
@@ -43,6 +46,12 @@ struct SwapArgs {
   uint32_t seg_local_vec[8];  // vectors of one rank's block of the segment
   FastDiv row_div, chunk_div;
 };
+
+// 16-byte store, nontemporal, written through L2 at agent scope. A store has
+// no result, so the compiler's wait for the loaded value before it stays.
+__device__ __forceinline__ void store_through(u32x4 *p, u32x4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1 nt" ::"v"(p), "v"(v) : "memory");
+}
 
 template <bool kToHead>
 __global__ void __launch_bounds__(kSwapThreads) swap_kernel(SwapArgs a) {
@@ -70,9 +79,9 @@ __global__ void __launch_bounds__(kSwapThreads) swap_kernel(SwapArgs a) {
   const uint32_t c_idx = (p * a.n + t) * a.chunk_vec + k;
   const uint32_t s_idx = t * a.row_vec + off;
   if (kToHead)
-    __builtin_nontemporal_store(__builtin_nontemporal_load(a.src + s_idx), a.dst + c_idx);
+    store_through(a.dst + c_idx, __builtin_nontemporal_load(a.src + s_idx));
   else
-    __builtin_nontemporal_store(__builtin_nontemporal_load(a.src + c_idx), a.dst + s_idx);
+    store_through(a.dst + s_idx, __builtin_nontemporal_load(a.src + c_idx));
 }
 
 }  // namespace
