@@ -497,6 +497,11 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
     toff[i] = (uint32_t)(d * a.Np * 2) + (((s & 7) ^ ((d >> 1) & 7)) << 4);
   }
   [[maybe_unused]] const TrOffsets tro = kTr ? tr_offsets(lane) : TrOffsets{};
+  // Byte offsets of this lane's 16-byte operand slots in a row tile, one per
+  // 16-wide d step (the second 32-row half adds 32 rows).
+  uint32_t rlo[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) rlo[ks] = (uint32_t)roff(l32, ks * 2 + hi32) * 2;
 
   // Tile t: query tiles from the last one down (every workgroup of a wave of
   // launches starts on the same tiles and walks them in step, so they are
@@ -569,13 +574,14 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
     // Query steps [C0, C1) of the update.
     auto dk_update = [&](const bf16_t *qts, auto c0, auto c1) __attribute__((always_inline)) {
       constexpr int C0 = decltype(c0)::value, C1 = decltype(c1)::value;
-      [[maybe_unused]] const uint32_t qa = lds_addr(qts);
+      [[maybe_unused]] TrBase qb;
+      if constexpr (kTr) qb = tr_base(lds_addr(qts), tro);
 #pragma unroll
       for (int c = C0; c < C1; ++c)
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
           bf16x8 aqt;
-          if constexpr (kTr) aqt = tr_frag(qa, tro, db, c);
+          if constexpr (kTr) aqt = tr_frag(qb, db, c);
           else aqt = as_bf16x8(*reinterpret_cast<const u32x4 *>(qts + tr_off(db * 32 + l32, c * 2 + hi32)));
           acc[db] = mfma32(aqt, sf[c], acc[db]);
         }
@@ -617,13 +623,15 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
         for (int q = 0; q < 2; ++q)
 #pragma unroll
           for (int i = 0; i < 16; ++i) x[q][i] = 0.f;
-        const bf16_t *rows = S ? qs : ds;
+        const uint32_t rb = lds_addr(S ? qs : ds);
+        uint32_t ra[C::KS];
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) ra[ks] = opaque(rb + rlo[ks]);
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
-            const bf16x8 ar =
-                as_bf16x8(*reinterpret_cast<const u32x4 *>(rows + roff(q * 32 + l32, ks * 2 + hi32)));
+            const bf16x8 ar = as_bf16x8(lds_read16(ra[ks] + q * 32 * D * 2));
             x[q] = mfma32(ar, xf[ks], x[q]);
           }
         pipeline_reads_mfma<2 * C::KS>();
@@ -637,11 +645,12 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
                 if (qi < qlo || qi >= qhi) x[q][i] = -INFINITY;
               }
           }
+          const uint32_t la = opaque(lds_addr(ls) + hi32 * 16);
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
-              const f32x4 l4 = *reinterpret_cast<const f32x4 *>(ls + q * 32 + gq * 8 + hi32 * 4);
+              const f32x4 l4 = lds_read16f(la + (q * 32 + gq * 8) * 4);
 #pragma unroll
               for (int e = 0; e < 4; ++e)
                 x[q][gq * 4 + e] = __builtin_amdgcn_exp2f(fmaf(x[q][gq * 4 + e], a.c, -l4[e]));
@@ -662,13 +671,14 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
       }
       if constexpr (S) {
         if (act) {
-          [[maybe_unused]] const uint32_t da = lds_addr(ds);
+          [[maybe_unused]] TrBase dbs;
+          if constexpr (kTr) dbs = tr_base(lds_addr(ds), tro);
 #pragma unroll
           for (int c = 0; c < 4; ++c)
 #pragma unroll
             for (int db = 0; db < C::DB; ++db) {
               bf16x8 adt;
-              if constexpr (kTr) adt = tr_frag(da, tro, db, c);
+              if constexpr (kTr) adt = tr_frag(dbs, db, c);
               else adt = as_bf16x8(*reinterpret_cast<const u32x4 *>(dts + tr_off(db * 32 + l32, c * 2 + hi32)));
               acc[db] = mfma32(adt, pf[c], acc[db]);
             }
@@ -681,6 +691,7 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
         }
         pend = act;
         if (act) {
+          const uint32_t la = opaque(lds_addr(ls) + (C::BQ + hi32 * 4) * 4);
 #pragma unroll
           for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -690,7 +701,7 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
 #pragma unroll
               for (int gq2 = 0; gq2 < 2; ++gq2) {
                 const int gq = jq * 2 + gq2;
-                const f32x4 d4 = *reinterpret_cast<const f32x4 *>(ls + C::BQ + q * 32 + gq * 8 + hi32 * 4);
+                const f32x4 d4 = lds_read16f(la + (q * 32 + gq * 8) * 4);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                   const int k = gq2 * 4 + e;  // fragment element
