@@ -201,7 +201,7 @@ int attn_fwd_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v, uin
                     int32_t causal, const int32_t *cu_seqlens, int32_t n_seqs,
                     int32_t max_seqlen, void *ws, size_t ws_bytes, hipStream_t stream);
 
-/* Workspace the backward pass needs: float32 D = rowsum(dO * O) and
+/* Workspace the backward pass needs: float32 -D, D = rowsum(dO * O), and
  * LSE*log2(e), [hq][roundup(N, 64)] each, then transposed copies of K, Q and
  * dO (hkv, hq and hq heads of d * roundup(N, 64) bf16), then two int32
  * arrays of roundup(N, 64) / 64 entries (the workgroup orders of the dK/dV
@@ -262,10 +262,10 @@ int attn_bwd_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
  * Long Sequence Training"): dq sums over keys, dk and dv over queries, so
  * each step is one pass that recomputes the scores it needs.
  *
- * attn_bwd_dq: fills ws (D, LSE*log2(e), at d = 64 the transposed copies of
+ * attn_bwd_dq: fills ws (-D, LSE*log2(e), at d = 64 the transposed copies of
  *   K, Q and dO, over packed documents the block orders of both steps) and
  *   writes dq.
- * attn_bwd_dkdv: dk and dv. It reads D, LSE*log2(e), (d = 64) the
+ * attn_bwd_dkdv: dk and dv. It reads -D, LSE*log2(e), (d = 64) the
  *   transposed copies of Q and dO and (packed documents) its key-block order
  *   from ws as left by attn_bwd_dq with the same arguments (not to be
  *   modified in between), and writes another region of ws: its float32

@@ -344,7 +344,7 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, scale: float, causal: bool = Tru
 
 def attn_bwd_dq(q, k, v, o, lse, dout, dq, scale: float, causal: bool = True, ws=None, cu_seqlens=None,
                 stream=None) -> None:
-    """First step of attn_bwd: D = rowsum(dout * o) and LSE*log2(e) into ws
+    """First step of attn_bwd: -D, D = rowsum(dout * o), and LSE*log2(e) into ws
     (with, at d = 64, the transposed copies and, over packed documents, both
     steps' block orders), and dq."""
     a = _Args("attn_bwd_dq")
@@ -360,7 +360,7 @@ def attn_bwd_dq(q, k, v, o, lse, dout, dq, scale: float, causal: bool = True, ws
 
 def attn_bwd_dkdv(q, k, v, lse, dout, dk, dv, scale: float, causal: bool = True, ws=None, cu_seqlens=None,
                   stream=None) -> None:
-    """Second step of attn_bwd: dk and dv, reading D, LSE, the transposed
+    """Second step of attn_bwd: dk and dv, reading -D, LSE, the transposed
     copies and the key-block order from ws (left there by attn_bwd_dq) and
     overwriting ws's dK/dV partial region (so concurrent calls need their own
     ws)."""

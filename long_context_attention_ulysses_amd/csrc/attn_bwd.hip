@@ -169,7 +169,7 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_bwd_dq_kernel(BwdArgs a
   const float delta = dpart + xor32(dpart);
   const float lse2 = row_ok ? a.lse[(int64_t)h * a.N + row] * kLog2e : 0.f;
   if (row_ok && hi32 == 0 && split == 0) {
-    a.delta[(int64_t)h * a.Np + row] = delta;
+    a.delta[(int64_t)h * a.Np + row] = -delta;  // the dK/dV kernel starts its dP accumulators at -D
     a.lse2[(int64_t)h * a.Np + row] = lse2;
   }
 
@@ -616,13 +616,29 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
       f32x16 x[2];
       bf16x8 pf[4];
       if constexpr (!S) {
+        // The dP accumulators start at -D of their query rows (the workspace
+        // holds -D), so the product leaves dP - D; read before the deferred
+        // dK update so that the reads complete under it.
+        if (act) {
+          const uint32_t la = opaque(lds_addr(ls) + (C::BQ + hi32 * 4) * 4);
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const f32x4 d4 = lds_read16f(la + (q * 32 + gq * 8) * 4);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) x[q][gq * 4 + e] = d4[e];
+            }
+        }
         if (pend) dk_update(qs_prev, IC0{}, ICP1{});
       }
       if (act) {
+        if constexpr (S) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
+          for (int q = 0; q < 2; ++q)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) x[q][i] = 0.f;
+            for (int i = 0; i < 16; ++i) x[q][i] = 0.f;
+        }
         const uint32_t rb = lds_addr(S ? qs : ds);
         uint32_t ra[C::KS];
 #pragma unroll
@@ -691,7 +707,6 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
         }
         pend = act;
         if (act) {
-          const uint32_t la = opaque(lds_addr(ls) + (C::BQ + hi32 * 4) * 4);
 #pragma unroll
           for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -701,13 +716,12 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
 #pragma unroll
               for (int gq2 = 0; gq2 < 2; ++gq2) {
                 const int gq = jq * 2 + gq2;
-                const f32x4 d4 = lds_read16f(la + (q * 32 + gq * 8) * 4);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                   const int k = gq2 * 4 + e;  // fragment element
                   const uint32_t wd = pw[k >> 1];
                   const float p = __uint_as_float((k & 1) ? (wd & 0xFFFF0000u) : (wd << 16));
-                  dsv[k] = p * (x[q][gq * 4 + e] - d4[e]);
+                  dsv[k] = p * x[q][gq * 4 + e];  // x holds dP - D
                 }
               }
               sf[q * 2 + jq] = cvt8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);

@@ -83,7 +83,7 @@ inline int dkdv_ksplit(int64_t N, int hkv) {
 // pass sums them.
 inline int dq_ksplit(int64_t N, int hq, int hkv) { return fwd_ksplit(N, hq, hkv); }
 
-// Backward workspace regions (byte offsets): D and LSE*log2(e) as float
+// Backward workspace regions (byte offsets): -D and LSE*log2(e) as float
 // [hq][pad64(N)], then K^T, Q^T, dO^T as contraction-ordered bf16 copies,
 // then the int32 orders of the dK/dV kernel's key blocks and of the dq
 // kernel's query blocks for packed documents (pad64(N) / 64 entries each),
