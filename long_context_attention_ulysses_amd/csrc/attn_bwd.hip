@@ -178,6 +178,9 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_bwd_dq_kernel(BwdArgs a
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+  f32x16 negd;  // starting value of the dP^T accumulators
+#pragma unroll
+  for (int i = 0; i < 16; ++i) negd[i] = -delta;
 
   // Key tiles of the block, and this workgroup's share of them [kt0, kt1).
   const int kta = (int)(kv_lo / C::BN);
@@ -235,12 +238,10 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_bwd_dq_kernel(BwdArgs a
     const bool need_mask = (t0 < w_lo_max) || (t0 + C::BN > w_hi_min);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s, dp;
+      // dP^T accumulates onto -D of the lane's row, leaving dP^T - D.
+      f32x16 s, dp = negd;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s[i] = 0.f;
-        dp[i] = 0.f;
-      }
+      for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
         const int off = roff(kb * 32 + l32, ks * 2 + hi32);
@@ -259,7 +260,7 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_bwd_dq_kernel(BwdArgs a
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float p = __builtin_amdgcn_exp2f(fmaf(s[i], a.c, -lse2));
-        s[i] = p * (dp[i] - delta);  // dS^T
+        s[i] = p * dp[i];  // dS^T
       }
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
