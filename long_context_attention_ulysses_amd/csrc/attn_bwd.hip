@@ -16,12 +16,14 @@
 // tiles stream into LDS with direct-to-LDS copies and are read with 16-byte
 // loads only.
 //   1. dq kernel, parallel over (query block, head): D and LSE*log2(e) for
-//      its rows (to the workspace), then per 64-key tile (3-stage ring):
+//      its rows (-D and LSE*log2(e) to the workspace), then per 64-key tile
+//      (3-stage ring):
 //      S^T = K Q^T, dP^T = V dO^T, P^T, dS^T, dQ^T += K^T dS^T
 //      (Q and dO stay in registers as B operands; a lane owns one query).
 //   2. dkdv kernel, parallel over (key block, KV head): loops over its
 //      64-query tiles from the last one down, the group's heads innermost
-//      (2-stage ring; concurrent workgroups walk the same tiles in step):
+//      (3-stage rings at d = 128; concurrent workgroups walk the same tiles
+//      in step):
 //      S = Q K^T, dP = dO V^T (K, V in registers; a lane owns one key),
 //      P, dS, dV^T += dO^T P, dK^T += Q^T dS.
 // Small problems (fewer than 512 blocks of either kernel) split each block's
@@ -33,11 +35,6 @@
 #include "attn_common.h"
 #include "uly_internal.h"
 
-// Tiles the d = 128 dK/dV kernel copies ahead (1: tile t+1's copies land
-// while tile t is computed).
-#ifndef ULY_DKDV_PF
-#define ULY_DKDV_PF 1
-#endif
 // MFMAs' worth of transposing reads the dK and dV updates keep in flight.
 #ifndef ULY_TR_LA
 #define ULY_TR_LA 4
@@ -388,18 +385,21 @@ struct DkvCfg {
 // kTr (d = 128): the dO^T and Q^T operands of the dV and dK products are
 // read from the Q and dO row tiles with transposing LDS reads (rt2 layout)
 // instead of being copied in from the transposed copies, which halves the
-// bytes copied into LDS per tile (Q and dO rows only). Q rows then live in a
+// bytes copied into LDS per tile (Q and dO rows only). Q rows then need a
 // 3-stage ring, since the deferred dK update reads tile t-1's while tile
-// t+1's arrive. Without kTr all four operands are copied (2-stage rings).
+// t+1's arrive; dO rows and LSE/D get three stages too, so that the tile
+// loop unrolls over the stages. Without kTr all four operands are copied
+// (2-stage rings).
 template <int D, bool kSplit, bool kTr>
 __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs a) {
   using C = DkvCfg<D>;
   static_assert(!kTr || D == 128, "the transposing-read layout is for d = 128");
-  // With kTr the copies of tile t + PF are issued at tile t; rows stay
-  // until their last reader: Q rows one tile longer (deferred dK update).
-  constexpr int PF = kTr ? ULY_DKDV_PF : 1;
-  constexpr int QST = kTr ? PF + 2 : 2;       // stages of the Q row ring
-  constexpr int DST = kTr ? PF + 1 : 2;       // stages of the dO row and LSE/D rings
+  // With kTr the copies of tile t + 1 are issued at tile t and every ring
+  // has three stages: Q rows stay one tile longer than dO rows (deferred dK
+  // update), and with equal rings the tile loop unrolls over the stages.
+  constexpr int PF = 1;
+  constexpr int QST = kTr ? 3 : 2;  // stages of the Q row ring
+  constexpr int DST = kTr ? 3 : 2;  // stages of the dO row and LSE/D rings
   constexpr int TT = kTr ? 8 : C::TILE;       // trans tiles (unused with kTr)
   __shared__ __align__(16) bf16_t qrow[QST][C::TILE];   // Q row tiles
   __shared__ __align__(16) bf16_t drow[DST][C::TILE];   // dO row tiles
@@ -575,14 +575,13 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
     // Query steps [C0, C1) of the update.
     auto dk_update = [&](const bf16_t *qts, auto c0, auto c1) __attribute__((always_inline)) {
       constexpr int C0 = decltype(c0)::value, C1 = decltype(c1)::value;
-      [[maybe_unused]] TrBase qb;
-      if constexpr (kTr) qb = tr_base(lds_addr(qts), tro);
+      [[maybe_unused]] const uint32_t qa = lds_addr(qts);
 #pragma unroll
       for (int c = C0; c < C1; ++c)
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
           bf16x8 aqt;
-          if constexpr (kTr) aqt = tr_frag(qb, db, c);
+          if constexpr (kTr) aqt = tr_frag(qa, tro, db, c);
           else aqt = as_bf16x8(*reinterpret_cast<const u32x4 *>(qts + tr_off(db * 32 + l32, c * 2 + hi32)));
           acc[db] = mfma32(aqt, sf[c], acc[db]);
         }
@@ -621,7 +620,7 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
         // holds -D), so the product leaves dP - D; read before the deferred
         // dK update so that the reads complete under it.
         if (act) {
-          const uint32_t la = opaque(lds_addr(ls) + (C::BQ + hi32 * 4) * 4);
+          const uint32_t la = lds_addr(ls) + (C::BQ + hi32 * 4) * 4;
 #pragma unroll
           for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -641,14 +640,11 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
             for (int i = 0; i < 16; ++i) x[q][i] = 0.f;
         }
         const uint32_t rb = lds_addr(S ? qs : ds);
-        uint32_t ra[C::KS];
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) ra[ks] = opaque(rb + rlo[ks]);
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
-            const bf16x8 ar = as_bf16x8(lds_read16(ra[ks] + q * 32 * D * 2));
+            const bf16x8 ar = as_bf16x8(lds_read16(rb + rlo[ks] + q * 32 * D * 2));
             x[q] = mfma32(ar, xf[ks], x[q]);
           }
         pipeline_reads_mfma<2 * C::KS>();
@@ -662,7 +658,7 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
                 if (qi < qlo || qi >= qhi) x[q][i] = -INFINITY;
               }
           }
-          const uint32_t la = opaque(lds_addr(ls) + hi32 * 16);
+          const uint32_t la = lds_addr(ls) + hi32 * 16;
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
 #pragma unroll
@@ -688,14 +684,13 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
       }
       if constexpr (S) {
         if (act) {
-          [[maybe_unused]] TrBase dbs;
-          if constexpr (kTr) dbs = tr_base(lds_addr(ds), tro);
+          [[maybe_unused]] const uint32_t da = lds_addr(ds);
 #pragma unroll
           for (int c = 0; c < 4; ++c)
 #pragma unroll
             for (int db = 0; db < C::DB; ++db) {
               bf16x8 adt;
-              if constexpr (kTr) adt = tr_frag(dbs, db, c);
+              if constexpr (kTr) adt = tr_frag(da, tro, db, c);
               else adt = as_bf16x8(*reinterpret_cast<const u32x4 *>(dts + tr_off(db * 32 + l32, c * 2 + hi32)));
               acc[db] = mfma32(adt, pf[c], acc[db]);
             }
@@ -736,12 +731,16 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
 #pragma unroll
       for (int p = 0; p < PF; ++p)
         if (tb + p < te) issue_rows(tb + p, qrow[p], drow[p], nullptr, lsb[p]);
-      for (int t = tb; t < te; ++t) {
-        const int rel = t - tb;
-        const int qi = rel % QST, di = rel % DST;
-        const int qn = (rel + PF) % QST, dn = (rel + PF) % DST;
-        tile(t, qrow[qi], drow[di], nullptr, lsb[di], qrow[qi == 0 ? QST - 1 : qi - 1], qrow[qn], drow[dn], nullptr,
-             lsb[dn], nullptr);
+      // Unrolled over the three stages, so that every LDS address in a tile
+      // is a constant plus a lane offset (the constant goes into the read's
+      // offset field; a stage picked at run time costs one VALU add per read).
+      static_assert(PF == 1 && QST == 3 && DST == 3, "the unrolled loop assumes 3-stage rings");
+      for (int t = tb; t < te; t += 3) {
+        tile(t, qrow[0], drow[0], nullptr, lsb[0], qrow[2], qrow[1], drow[1], nullptr, lsb[1], nullptr);
+        if (t + 1 < te)
+          tile(t + 1, qrow[1], drow[1], nullptr, lsb[1], qrow[0], qrow[2], drow[2], nullptr, lsb[2], nullptr);
+        if (t + 2 < te)
+          tile(t + 2, qrow[2], drow[2], nullptr, lsb[2], qrow[1], qrow[0], drow[0], nullptr, lsb[0], nullptr);
       }
       // The last tile's dK update (its Q rows stay in place: nothing more is copied).
       if constexpr (!S) {

@@ -138,48 +138,12 @@ __device__ __forceinline__ bf16x8 tr_frag(uint32_t tile, const TrOffsets &t, int
   return as_bf16x8(v);
 }
 
-// A value the compiler takes as unknown (kept in a VGPR). A tile's LDS
-// addresses are formed once per tile as opaque(stage base + lane offset);
-// every read then adds only a constant, which goes into the instruction's
-// offset field. Without this the compiler re-associates the sums into a
-// scalar part per read and spends one VALU add on every read.
-__device__ __forceinline__ uint32_t opaque(uint32_t x) {
-  asm("" : "+v"(x));
-  return x;
-}
-
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 
 // 16-byte LDS reads at LDS byte address `addr` (16-byte aligned).
 __device__ __forceinline__ u32x4 lds_read16(uint32_t addr) { return *(const lds_u32x4 *)(uintptr_t)addr; }
 __device__ __forceinline__ f32x4 lds_read16f(uint32_t addr) { return *(const lds_f32x4 *)(uintptr_t)addr; }
-
-// Per-lane LDS addresses of the transposing reads of one row tile (tile +
-// TrOffsets), formed once per tile; step c adds the constant 4096 c.
-struct TrBase {
-  uint32_t a[2][4];
-};
-
-__device__ __forceinline__ TrBase tr_base(uint32_t tile, const TrOffsets &t) {
-  TrBase b;
-#pragma unroll
-  for (int r = 0; r < 2; ++r)
-#pragma unroll
-    for (int db = 0; db < 4; ++db) b.a[r][db] = opaque(tile + t.off[r][db]);
-  return b;
-}
-
-__device__ __forceinline__ bf16x8 tr_frag(const TrBase &b, int db, int c) {
-  const u32x2 lo = ds_read_tr(b.a[0][db] + 4096 * c);
-  const u32x2 hi = ds_read_tr(b.a[1][db] + 4096 * c);
-  u32x4 v;
-  v[0] = lo[0];
-  v[1] = lo[1];
-  v[2] = hi[0];
-  v[3] = hi[1];
-  return as_bf16x8(v);
-}
 
 // Buffer resource (four SGPRs) over the `bytes` bytes at `base`: buffer
 // loads at byte offsets >= bytes return zeros (raw buffer, stride 0).
