@@ -506,15 +506,26 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
 
   // Tile t: query tiles from the last one down (every workgroup of a wave of
   // launches starts on the same tiles and walks them in step, so they are
-  // shared through L2), the group's heads innermost.
-  auto tile_head = [&](int t) { return g * a.G + t % a.G; };
-  auto tile_u0 = [&](int t) { return (uint32_t)(qt1_ - 1 - t / a.G) * C::BQ; };
+  // shared through L2), the group's heads innermost. A cursor holds tile t's
+  // head within the group and query tile (counted from the last one); the
+  // next tile's comes from a compare and two selects (dividing t by G, known
+  // only at run time, costs about 15 scalar instructions per tile).
+  struct TileCur {
+    int hh, qi;
+  };
+  auto cur_at = [&](int t) { return TileCur{t % a.G, t / a.G}; };
+  auto next_cur = [&](TileCur c) {
+    const bool wrap = c.hh + 1 == a.G;
+    return TileCur{wrap ? 0 : c.hh + 1, wrap ? c.qi + 1 : c.qi};
+  };
+  auto tile_head = [&](TileCur c) { return g * a.G + c.hh; };
+  auto tile_u0 = [&](TileCur c) { return (uint32_t)(qt1_ - 1 - c.qi) * C::BQ; };
 
   // Copies of tile t: Q and dO row tiles, the dO^T trans tile (without kTr)
   // and the tile's LSE*log2e and D (issue_rows); the Q^T trans tile
   // (issue_qt, without kTr), which is needed one tile later than the others
   // (see the schedule below).
-  auto issue_rows = [&](int t, bf16_t *qs, bf16_t *ds, bf16_t *dts, float *ls) {
+  auto issue_rows = [&](TileCur t, bf16_t *qs, bf16_t *ds, bf16_t *dts, float *ls) {
     const int h = tile_head(t);
     const uint32_t u0 = tile_u0(t);
     // Q and dO rows of head h from row u0 to the end of row N-1 (rows >= N
@@ -542,14 +553,14 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
       dma4(make_rsrc(src + u0, (uint32_t)((a.N - u0) * 4)), lane * 4, 0, ls + w * C::BQ);
     }
   };
-  auto issue_qt = [&](int t, bf16_t *qts) {
+  auto issue_qt = [&](TileCur t, bf16_t *qts) {
     const int h = tile_head(t);
     const uint32_t u0 = tile_u0(t);
     const BufRes qtr = make_rsrc(a.qt + (int64_t)h * D * a.Np, (uint32_t)(D * a.Np * 2));
 #pragma unroll
     for (int i = 0; i < C::NI / C::NW; ++i) dma16(qtr, toff[i], u0 * 2, qts + (w + i * C::NW) * 512);
   };
-  auto active = [&](int t) {
+  auto active = [&](TileCur t) {
     const int64_t u0 = tile_u0(t);
     return wave_valid && u0 < w_hi && u0 + C::BQ > w_lo;
   };
@@ -594,7 +605,8 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
 
     // qs_prev: Q^T(t-1) trans tile, or (kTr) tile t-1's Q rows.
     // qs_n, ds_n, ls_n: stages for tile t + PF's copies.
-    auto tile = [&](int t, const bf16_t *qs, const bf16_t *ds, const bf16_t *dts, const float *ls,
+    // tc, tn: cursors of tiles t and t + 1.
+    auto tile = [&](int t, TileCur tc, TileCur tn, const bf16_t *qs, const bf16_t *ds, const bf16_t *dts, const float *ls,
                     const bf16_t *qs_prev, bf16_t *qs_n, bf16_t *ds_n, bf16_t *dts_n, float *ls_n,
                     bf16_t *qts_n) __attribute__((always_inline)) {
       if constexpr (kTr) {
@@ -610,9 +622,9 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
         wait_vmcnt<C::NI / C::NW>();
       }
       barrier();
-      if (t + PF < te) issue_rows(t + PF, qs_n, ds_n, dts_n, ls_n);
-      const int64_t u0 = tile_u0(t);
-      const bool act = active(t);
+      if (t + PF < te) issue_rows(tn, qs_n, ds_n, dts_n, ls_n);
+      const int64_t u0 = tile_u0(tc);
+      const bool act = active(tc);
       f32x16 x[2];
       bf16x8 pf[4];
       if constexpr (!S) {
@@ -680,7 +692,7 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
       }
       lds_barrier();
       if constexpr (!kTr) {
-        if (t + 1 < te) issue_qt(t + 1, qts_n);
+        if (t + 1 < te) issue_qt(tn, qts_n);
       }
       if constexpr (S) {
         if (act) {
@@ -728,32 +740,37 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
 
     wait_vmcnt<0>();  // K or V fragments loaded: only tile copies are counted below
     if constexpr (kTr) {
-#pragma unroll
-      for (int p = 0; p < PF; ++p)
-        if (tb + p < te) issue_rows(tb + p, qrow[p], drow[p], nullptr, lsb[p]);
       // Unrolled over the three stages, so that every LDS address in a tile
       // is a constant plus a lane offset (the constant goes into the read's
       // offset field; a stage picked at run time costs one VALU add per read).
       static_assert(PF == 1 && QST == 3 && DST == 3, "the unrolled loop assumes 3-stage rings");
+      TileCur c0 = cur_at(tb);
+      if (tb < te) issue_rows(c0, qrow[0], drow[0], nullptr, lsb[0]);
       for (int t = tb; t < te; t += 3) {
-        tile(t, qrow[0], drow[0], nullptr, lsb[0], qrow[2], qrow[1], drow[1], nullptr, lsb[1], nullptr);
+        const TileCur c1 = next_cur(c0), c2 = next_cur(c1), c3 = next_cur(c2);
+        tile(t, c0, c1, qrow[0], drow[0], nullptr, lsb[0], qrow[2], qrow[1], drow[1], nullptr, lsb[1], nullptr);
         if (t + 1 < te)
-          tile(t + 1, qrow[1], drow[1], nullptr, lsb[1], qrow[0], qrow[2], drow[2], nullptr, lsb[2], nullptr);
+          tile(t + 1, c1, c2, qrow[1], drow[1], nullptr, lsb[1], qrow[0], qrow[2], drow[2], nullptr, lsb[2], nullptr);
         if (t + 2 < te)
-          tile(t + 2, qrow[2], drow[2], nullptr, lsb[2], qrow[1], qrow[0], drow[0], nullptr, lsb[0], nullptr);
+          tile(t + 2, c2, c3, qrow[2], drow[2], nullptr, lsb[2], qrow[1], qrow[0], drow[0], nullptr, lsb[0], nullptr);
+        c0 = c3;
       }
       // The last tile's dK update (its Q rows stay in place: nothing more is copied).
       if constexpr (!S) {
         if (pend) dk_update(qrow[(te - 1 - tb) % QST], IC0{}, IC4{});
       }
     } else {
+      TileCur c0 = cur_at(tb);
       if (tb < te) {
-        issue_rows(tb, qrow[0], drow[0], dtt[0], lsb[0]);
-        issue_qt(tb, qtt[0]);
+        issue_rows(c0, qrow[0], drow[0], dtt[0], lsb[0]);
+        issue_qt(c0, qtt[0]);
       }
       for (int t = tb; t < te; t += 2) {
-        tile(t, qrow[0], drow[0], dtt[0], lsb[0], qtt[1], qrow[1], drow[1], dtt[1], lsb[1], qtt[1]);
-        if (t + 1 < te) tile(t + 1, qrow[1], drow[1], dtt[1], lsb[1], qtt[0], qrow[0], drow[0], dtt[0], lsb[0], qtt[0]);
+        const TileCur c1 = next_cur(c0), c2 = next_cur(c1);
+        tile(t, c0, c1, qrow[0], drow[0], dtt[0], lsb[0], qtt[1], qrow[1], drow[1], dtt[1], lsb[1], qtt[1]);
+        if (t + 1 < te)
+          tile(t + 1, c1, c2, qrow[1], drow[1], dtt[1], lsb[1], qtt[0], qrow[0], drow[0], dtt[0], lsb[0], qtt[0]);
+        c0 = c2;
       }
       // The last tile's dK update: its Q^T copy is complete once every wave
       // has waited for its own part of it.
