@@ -39,10 +39,6 @@
 #ifndef ULY_TR_LA
 #define ULY_TR_LA 4
 #endif
-// Read-ahead hint for the dq kernel's transposing reads (0: none).
-#ifndef ULY_DQ_HINT
-#define ULY_DQ_HINT 0
-#endif
 // 16-query steps of the deferred dK update done in phase 1 (the rest in phase 2).
 #ifndef ULY_DK_P1
 #define ULY_DK_P1 4
@@ -247,6 +243,10 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_bwd_dq_kernel(BwdArgs a
         s = mfma32(ak, qf[ks], s);
         dp = mfma32(av, dof[ks], dp);
       }
+      // Reads issued ahead of their MFMAs (with all 256 registers in use the
+      // compiler otherwise waits for every read right after issuing it;
+      // asking for more than 2 reads ahead makes it give up entirely).
+      pipeline_reads_mfma<2 * C::KS, 2>();
       if (need_mask) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -272,9 +272,7 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_bwd_dq_kernel(BwdArgs a
           acc[db] = mfma32(ak, dsf, acc[db]);
         }
       }
-#if ULY_DQ_HINT
       if constexpr (kTr) pipeline_reads_mfma_n<2 * C::DB, 2, 2>();
-#endif
     }
   };
 
