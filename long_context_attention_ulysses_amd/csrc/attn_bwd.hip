@@ -660,12 +660,13 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
         pipeline_reads_mfma<2 * C::KS>();
         if constexpr (S) {
           if ((u0 < w_lo_max) || (u0 + C::BQ > w_hi_min)) {
+            const RelRange rr = rel_range(qlo, qhi, u0, hi32 * 4);
 #pragma unroll
             for (int q = 0; q < 2; ++q)
 #pragma unroll
               for (int i = 0; i < 16; ++i) {
-                const int64_t qi = u0 + q * 32 + (i >> 2) * 8 + hi32 * 4 + (i & 3);
-                if (qi < qlo || qi >= qhi) x[q][i] = -INFINITY;
+                const int e = q * 32 + (i >> 2) * 8 + (i & 3);
+                if (e < rr.lo || e >= rr.hi) x[q][i] = -INFINITY;
               }
           }
           const uint32_t la = lds_addr(ls) + hi32 * 16;

@@ -280,6 +280,20 @@ __device__ __forceinline__ void pipeline_reads_mfma_n() {
   __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
 }
 
+// A lane's token range [lo, hi) relative to a 64-token tile at t0, for
+// masking the tile's elements: element offset E (0..63) is inside iff
+// lo <= E - lane_off < hi. The offsets are clamped to [-1, 65] first, which
+// keeps every comparison with E in 0..63, so they fit in 32 bits.
+struct RelRange {
+  int lo, hi;
+};
+__host__ __device__ __forceinline__ RelRange rel_range(int64_t lo, int64_t hi, int64_t t0, int lane_off) {
+  int64_t l = lo - t0, h = hi - t0;
+  l = l < -1 ? -1 : (l > 65 ? 65 : l);
+  h = h < -1 ? -1 : (h > 65 ? 65 : h);
+  return RelRange{(int)l - lane_off, (int)h - lane_off};
+}
+
 // Value of lane l ^ 32.
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 

@@ -195,12 +195,13 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_fwd_kernel(FwdArgs a) {
     }
     pipeline_reads_mfma<2 * C::KS>();
     if ((t0 < w_lo_max) || (t0 + C::BN > w_hi_min)) {
+      const RelRange rr = rel_range(rlo, rhi, t0, hi32 * 4);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int64_t key = t0 + kb * 32 + (i >> 2) * 8 + hi32 * 4 + (i & 3);
-          if (key < rlo || key >= rhi) s[kb][i] = -INFINITY;
+          const int e = kb * 32 + (i >> 2) * 8 + (i & 3);
+          if (e < rr.lo || e >= rr.hi) s[kb][i] = -INFINITY;
         }
     }
     float mx = -INFINITY;

@@ -1,6 +1,8 @@
 // Host build of the attention kernels' key/query range helpers: every range
 // they return lies in [0, N) with lo <= hi, for valid and invalid
-// cu_seqlens tables alike; for valid tables it is the document's range.
+// cu_seqlens tables alike; for valid tables it is the document's range. The
+// tile-relative bounds the masks compare in 32 bits select the same
+// elements as the 64-bit ranges.
 #include <stdio.h>
 
 #include "attn_common.h"
@@ -66,6 +68,27 @@ int main() {
     const KeyRange k = uly::key_range(nullptr, 0, 16, 1, t), q = uly::query_range(nullptr, 0, 16, 1, t);
     if (k.lo != 0 || k.hi != t + 1 || q.lo != t || q.hi != 16) ++bad;
   }
+  // tile-relative 32-bit bounds used for masking: for every element offset
+  // E = e + lane_off of a 64-token tile at t0, lo <= t0 + E < hi exactly when
+  // rr.lo <= e < rr.hi, also for ranges far outside the tile
+  const int64_t far = (int64_t)1 << 40;
+  const int64_t ends[] = {-far, -1, 0, 1, 3, 4, 5, 31, 32, 33, 60, 63, 64, 65, 66, 67, 68, 130, far};
+  for (const int64_t t0 : {(int64_t)0, (int64_t)64, (int64_t)4096 * 64, far})
+    for (const int64_t dl : ends)
+      for (const int64_t dh : ends)
+        for (int lane_off = 0; lane_off <= 4; lane_off += 4) {
+          const int64_t lo = t0 + dl, hi = t0 + dh;
+          const uly::RelRange rr = uly::rel_range(lo, hi, t0, lane_off);
+          for (int e = 0; e + lane_off < 64; ++e) {
+            const int64_t tok = t0 + e + lane_off;
+            const bool in_range = tok >= lo && tok < hi, in_rel = e >= rr.lo && e < rr.hi;
+            if (in_range != in_rel) {
+              printf("rel_range differs: t0=%lld lo=%lld hi=%lld lane_off=%d e=%d\n", (long long)t0, (long long)lo,
+                     (long long)hi, lane_off, e);
+              ++bad;
+            }
+          }
+        }
   printf("%s\n", bad ? "FAIL" : "OK");
   return bad ? 1 : 0;
 }
