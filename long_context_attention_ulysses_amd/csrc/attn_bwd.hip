@@ -563,8 +563,8 @@ __global__ void __launch_bounds__(DkvCfg<D>::NT, 1) attn_bwd_dkdv_kernel(BwdArgs
     return wave_valid && u0 < w_hi && u0 + C::BQ > w_lo;
   };
 
-  // Schedule of tile t (stage t % 2 of every ring, t % 3 of the Q rows with
-  // kTr; B = ring barrier, X = P hand-over barrier):
+  // Schedule of tile t (stage t % 3 of every ring with kTr, t % 2 without;
+  // B = ring barrier, X = P hand-over barrier):
   //   wait for tile t's copies (without kTr: all but Q^T(t)), B, issue_rows(t + 1)
   //   phase 1  S role:  S(t), P(t), P -> LDS
   //            dP role: dK += Q^T(t-1) dS(t-1), dP(t)
