@@ -47,12 +47,6 @@ struct SwapArgs {
   FastDiv row_div, chunk_div;
 };
 
-// 16-byte store, nontemporal, written through L2 at agent scope. A store has
-// no result, so the compiler's wait for the loaded value before it stays.
-__device__ __forceinline__ void store_through(u32x4 *p, u32x4 v) {
-  asm volatile("global_store_dwordx4 %0, %1, off sc1 nt" ::"v"(p), "v"(v) : "memory");
-}
-
 template <bool kToHead>
 __global__ void __launch_bounds__(kSwapThreads) swap_kernel(SwapArgs a) {
   const uint32_t i = blockIdx.x * kSwapThreads + threadIdx.x;

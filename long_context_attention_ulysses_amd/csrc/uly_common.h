@@ -14,6 +14,16 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// 16-byte store, nontemporal, written through L2 at agent scope (sc1), for
+// streams whose output is not read back soon (the swaps, the ring merge and
+// gradient sum): no dirty lines are left in the XCD's L2 for later
+// eviction. One line of inline assembly, since no builtin sets the scope
+// bit; a store has no result, so the compiler's wait for the stored value
+// stays in place.
+__device__ __forceinline__ void store_through(void *p, u32x4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1 nt" ::"v"(p), "v"(v) : "memory");
+}
+
 // Unsigned division of 32-bit values by a runtime divisor via a
 // multiply-high and a shift (Granlund & Montgomery, "Division by Invariant
 // Integers using Multiplication", PLDI 1994, round-up variant with a 33-bit
