@@ -511,3 +511,82 @@ def test_split_backward_equals_attn_bwd():
         torch.cuda.synchronize()
         assert np.array_equal(host(dq), ref[0])
         assert np.array_equal(host(dkv)[:, :hkv], ref[1]) and np.array_equal(host(dkv)[:, hkv:], ref[2])
+
+
+def _align256(n):
+    return (n + 255) // 256 * 256
+
+
+def _expected_order(cu, N, causal, bs, key_blocks):
+    """Blocks of bs rows sorted by decreasing work, ties in id order; the work
+    of a block is the number of 64-token tiles its rows' visible range spans
+    (keys seen by its queries, or queries that see its keys). Visibility:
+    same document, and j <= i under the causal mask."""
+    t = np.arange(N, dtype=np.int64)
+    doc = np.searchsorted(cu, t, side="right") - 1
+    start, end = cu[doc].astype(np.int64), cu[doc + 1].astype(np.int64)
+    if key_blocks:  # queries that see key j: [j or doc start, doc end)
+        lo, hi = (t if causal else start), end
+    else:           # keys query i sees: [doc start, i + 1 or doc end)
+        lo, hi = start, (t + 1 if causal else end)
+    nb = (N + bs - 1) // bs
+    first = np.arange(nb) * bs
+    last = np.minimum(first + bs, N) - 1
+    work = (hi[last] + 63) // 64 - lo[first] // 64
+    return np.array(sorted(range(nb), key=lambda i: (-int(work[i]), i)), dtype=np.int32)
+
+
+@pytest.mark.parametrize("case", ["varlen-64k", "ties-ragged", "ties-ragged-full", "d64-g2"])
+def test_packed_block_orders_sort_blocks_by_work(case):
+    """Over packed documents the forward, dq and dK/dV kernels take their
+    blocks in the order a sorting pass leaves in the workspace (its regions
+    as the header lays them out): all blocks, by decreasing tile work, equal
+    work in id order. Index work, so compared exactly."""
+    causal = case != "ties-ragged-full"
+    if case == "varlen-64k":
+        cu = workloads.cu_seqlens(workloads.WORKLOADS["varlen"])
+        N, hq, hkv, d = int(cu[-1]), 8, 2, 128
+    elif case == "d64-g2":
+        N, hq, hkv, d = 3001, 4, 2, 64
+        cu = workloads.random_cu_seqlens(N, seed=77, lo=1, hi=900)
+    else:  # many short documents: most blocks tie
+        N, hq, hkv, d = 1000, 8, 2, 128
+        cu = workloads.random_cu_seqlens(N, seed=76, lo=1, hi=70)
+    hpw = 4 if (hq // hkv) % 4 == 0 else 2 if (hq // hkv) % 2 == 0 else 1
+    q_bs, k_bs = 256 // hpw, 128
+    np64 = (N + 63) // 64 * 64
+    nq, nk = (N + q_bs - 1) // q_bs, (N + k_bs - 1) // k_bs
+    print("block orders: %s N=%d hq=%d hkv=%d d=%d docs=%d" % (case, N, hq, hkv, d, len(cu) - 1), flush=True)
+
+    g = torch.Generator(device="cuda").manual_seed(5)
+    qkv = (torch.randn((N, hq + 2 * hkv, d), generator=g, device="cuda") * 0.5).to(torch.bfloat16)
+    q, k, v = qkv[:, :hq], qkv[:, hq:hq + hkv], qkv[:, hq + hkv:]
+    dy = torch.randn((N, hq, d), generator=g, device="cuda").to(torch.bfloat16)
+    cu_dev = torch.tensor(cu, dtype=torch.int32, device="cuda")
+    scale = 1 / np.sqrt(d)
+
+    fws = torch.zeros(uly.attn_fwd_workspace_bytes(N, hq, hkv, d), dtype=torch.uint8, device="cuda")
+    o = torch.empty((N, hq, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((hq, N), dtype=torch.float32, device="cuda")
+    uly.attn_fwd(q, k, v, o, lse, scale, causal, cu_dev, int(np.max(np.diff(cu))), ws=fws)
+    bws = torch.zeros(uly.attn_bwd_workspace_bytes(N, hq, hkv, d), dtype=torch.uint8, device="cuda")
+    dq = torch.empty((N, hq, d), dtype=torch.bfloat16, device="cuda")
+    uly.attn_bwd_dq(q, k, v, o, lse, dy, dq, scale, causal, bws, cu_dev)
+    torch.cuda.synchronize()
+
+    # Forward: the order is the workspace's last region.
+    fo = fws[fws.numel() - _align256(np64 // 64 * 4):].cpu().numpy().view(np.int32)[:nq]
+    # Backward: -D, LSE*log2(e), K^T, Q^T, dO^T, then the key-block and
+    # query-block orders.
+    korder_at = (2 * _align256(hq * np64 * 4) + _align256(hkv * d * np64 * 2)
+                 + 2 * _align256(hq * d * np64 * 2))
+    qorder_at = korder_at + _align256(np64 // 64 * 4)
+    b = bws.cpu().numpy()
+    ko = b[korder_at:korder_at + nk * 4].view(np.int32)
+    qo = b[qorder_at:qorder_at + nq * 4].view(np.int32)
+
+    want_q = _expected_order(cu, N, causal, q_bs, key_blocks=False)
+    want_k = _expected_order(cu, N, causal, k_bs, key_blocks=True)
+    assert np.array_equal(fo, want_q)
+    assert np.array_equal(qo, want_q)
+    assert np.array_equal(ko, want_k)
