@@ -159,7 +159,7 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_bwd_dq_kernel(BwdArgs a
       dpart = fmaf(__uint_as_float(vd[e] & 0xFFFF0000u), __uint_as_float(vo[e] & 0xFFFF0000u), dpart);
     }
   }
-  const float delta = dpart + xor32(dpart);
+  const float delta = sum_halves(dpart);
   const float lse2 = row_ok ? a.lse[(int64_t)h * a.N + row] * kLog2e : 0.f;
   if (row_ok && hi32 == 0 && split == 0) {
     a.delta[(int64_t)h * a.Np + row] = -delta;  // the dK/dV kernel starts its dP accumulators at -D

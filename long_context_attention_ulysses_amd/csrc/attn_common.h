@@ -295,7 +295,20 @@ __host__ __device__ __forceinline__ RelRange rel_range(int64_t lo, int64_t hi, i
 }
 
 // Value of lane l ^ 32.
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Max and sum of x over lanes l and l ^ 32, in every lane of the wave.
+// v_permlane32_swap trades the upper 32 lanes of its first operand for the
+// lower 32 of its second; with x in both, each lane ends up holding x of
+// both halves (its own and its partner's) in registers, where a shuffle
+// goes through LDS and waits for every LDS access in flight. max and +
+// commute, so both lanes of a pair get the same bits.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Document containing token t: largest b with cu[b] <= t (cu strictly increasing).
 __host__ __device__ __forceinline__ int doc_of(const int32_t *cu, int n_seqs, int64_t t) {

@@ -209,7 +209,7 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_fwd_kernel(FwdArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = fmaxf(mx, xor32(mx));
+    mx = max_halves(mx);
     // The running max m only moves when this tile's max exceeds it by more
     // than kMaxSlack (log2 units), so p = exp2(s*c - m) stays below
     // 2^kMaxSlack; O and l are rescaled only when some lane of the wave moves
@@ -278,7 +278,7 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_fwd_kernel(FwdArgs a) {
 
   // Epilogue: O = O^T / l, LSE = (m + log2 l) * ln 2; with a split, the
   // unnormalised O^T, m and l of this share of the keys.
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = sum_halves(l_run);
   if constexpr (kSplit) {
     if (row_ok) {
       float *orow = a.opart + (((int64_t)split * a.N + row) * a.hq + h) * D;
