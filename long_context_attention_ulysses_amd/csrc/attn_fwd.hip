@@ -227,7 +227,7 @@ __global__ void __launch_bounds__(HPW * RB * 64, 1) attn_fwd_kernel(FwdArgs a) {
         for (int i = 0; i < 16; ++i) acc_o[db][i] *= alpha;
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    float rs = 0.f;
+    float rs = -0.f;  // -0 + p is p exactly, so the first add folds away
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
